@@ -1,0 +1,119 @@
+/*
+ * Reference ("oracle") implementation of the routed-expert FFN layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This code is a plain, slow, single-threaded
+ * restatement of what the layer computes, used to check the GPU library.
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load it.  It shares no source, header, table or helper with the GPU
+ * library, and the GPU library never calls it.
+ *
+ * What the layer computes (sources are the three web pages this project
+ * follows):
+ *  - "Optimizing on-device inference for Apple Silicon" (Perplexity),
+ *    section "Qwen creates three distinct workload shapes": a router scores
+ *    every routed expert and picks eight of them per token; one shared expert
+ *    processes every token.
+ *  - same page, section "Reduce intermediate and state traffic": an expert is
+ *    two input projections followed by a gated activation (gate/up), then an
+ *    output projection whose result is scaled by the routing score and added
+ *    to the shared expert's result.
+ *  - same page, section "Keep expert routing on the GPU": after selection the
+ *    assignments are counted per expert (histogram), the counts are turned
+ *    into start offsets (prefix scan) and the rows are scattered into
+ *    per-expert groups.
+ *  - "Three ways to boost mixture-of-experts inference on NVIDIA DGX Spark",
+ *    sections "Why decoding was slow in the first place" and "Optimization 1":
+ *    512 routed experts, eight per token, a shared expert, hidden size 2560,
+ *    expert intermediate size 768, expert weights in MXFP4.
+ *
+ * Readings taken where the pages are silent (each is also listed with the
+ * design notes of the repository):
+ *  R1 logits l[t][e] = sum_h x[t][h] * Wr[e][h] + bias[t][e], computed in
+ *     double and rounded once to fp32; selection is taken on these fp32 keys.
+ *  R2 top-k = the k largest logits, ties to the lower expert index, listed in
+ *     descending logit order (ascending index among equals).
+ *  R3 p = softmax over all E logits (double); the k combine weights are the
+ *     selected p renormalised to sum 1.
+ *  R4 expert FFN (SwiGLU): g = Wg x, u = Wu x, a_i = silu(g_i) * u_i with
+ *     silu(z) = z / (1 + exp(-z)), o = Wd a.  No biases, no clamp.
+ *  R5 y = sum_j w_j * o_j (in rank order j = 0..k-1) + S(x), where S is the
+ *     shared expert's FFN with weight 1 (no shared gate).  I_shared = 0 means
+ *     no shared expert.
+ *  R6 weight layout is [out][in] (rows along the output, the reduction index
+ *     contiguous).  MXFP4: two e2m1 codes per byte, the even element in the
+ *     low nibble; one e8m0 scale byte per 32 consecutive elements of a row.
+ *     e2m1 and e8m0 follow the OCP Microscaling (MX) v1.0 specification.
+ *  R7 routing plan: per-expert counts, exclusive offsets, and slots
+ *     (slot = t*k + j) ordered by expert by a stable counting sort.
+ *
+ * All arithmetic is double precision.  Inputs (fp32, bf16, MXFP4) are decoded
+ * exactly to double.
+ */
+#ifndef ORACLE_MOE_H
+#define ORACLE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element encodings understood by the oracle. */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2 };
+
+typedef struct {
+  int32_t T, H, E, k, I, I_shared;
+  int32_t act_dtype;    /* ORC_F32 | ORC_BF16 */
+  int32_t expert_dtype; /* ORC_F32 | ORC_BF16 | ORC_MXFP4 */
+  int32_t shared_dtype; /* ORC_F32 | ORC_BF16 */
+} orc_shape;
+
+typedef struct {
+  const float *router_w;     /* [E][H] */
+  const float *router_bias;  /* NULL, [E] (stride 0) or [T][E] (stride E) */
+  int64_t bias_t_stride;
+  const void *gate, *up, *down;          /* [E][I][H], [E][I][H], [E][H][I] */
+  const uint8_t *gate_s, *up_s, *down_s; /* MXFP4 scales [E][I][H/32] ... */
+  const void *sh_gate, *sh_up, *sh_down; /* [Is][H], [Is][H], [H][Is] */
+} orc_weights;
+
+/* Scalar decoders (exact). */
+double orc_bf16_to_double(uint16_t bits);
+double orc_e2m1_to_double(uint8_t nibble);   /* low 4 bits used */
+double orc_e8m0_to_double(uint8_t bits);     /* 2^(bits-127); NaN for 0xFF */
+
+/* Element (row r, column c) of matrix `mat` of a stacked [n_mat][rows][cols]
+ * weight array in the given encoding (cols is the reduction dimension). */
+double orc_weight(const void *base, const uint8_t *scales, int dtype,
+                  int64_t mat, int64_t rows, int64_t cols, int64_t r, int64_t c);
+
+/* R1: router logits for all tokens, fp32 [T][E]. */
+int orc_logits(const orc_shape *s, const void *x, const orc_weights *w,
+               float *logits);
+
+/* R2 + R3 for one token: ids[k] and combine weights w[k] from fp32 logits. */
+int orc_select(const float *logits_row, int E, int k, int32_t *ids, double *w);
+
+/* R7: counts[E], offsets[E+1], sorted_slot[T*k] from ids[T][k]. */
+int orc_plan(const int32_t *ids, int T, int k, int E, int32_t *counts,
+             int32_t *offsets, int32_t *sorted_slot);
+
+/* One SwiGLU FFN (R4) on one token vector: rows Wg/Wu [I][H], Wd [H][I]. */
+int orc_ffn(const double *xv, int H, int I, const void *g, const void *u,
+            const void *d, const uint8_t *gs, const uint8_t *us,
+            const uint8_t *ds, int dtype, int64_t mat, double *out);
+
+/* R4 + R5 with the routing given: y[T][H] (double). */
+int orc_forward_with_routing(const orc_shape *s, const void *x,
+                             const orc_weights *w, const int32_t *ids,
+                             const double *cw, double *y);
+
+/* Whole layer: R1..R5.  ids/cw/logits may be NULL. */
+int orc_forward(const orc_shape *s, const void *x, const orc_weights *w,
+                double *y, int32_t *ids, double *cw, float *logits);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
