@@ -1,0 +1,216 @@
+"""Benchmark of the routed-expert FFN layer (libmoe) on one MI355X.
+
+One step = one moe_forward call (router -> selection -> expert SwiGLU -> combine with the
+shared expert) on one batch of synthetic tokens.  The default workload is batch-1 decode
+with Qwen-style shapes: T=1, hidden 2048, 256 routed experts top-8 + 1 shared, expert and
+shared intermediate 512, bf16 weights and activations, fp32 router; 48 independently drawn
+layers are rotated call by call so that no layer's weights stay in the 256 MiB Infinity
+Cache.  Other workloads (--workload): ling_verify (T=4, H=2560, E=512, I=768, d distinct
+experts), ling_mxfp4 (same with MXFP4 experts; T=1 or 4), qwen_prefill (T=4096).
+
+Prints ONE JSON line: value = tokens/s of the whole layer (inputs resident in HBM), the
+roofline of the dominant kernel (its algorithmic bytes per launch over its mean launch time
+from HIP events on the launch stream), and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def workload_spec(name, T_override=None, d=32):
+    if name == "qwen_decode":
+        return dict(T=T_override or 1, H=2048, E=256, k=8, I=512, I_shared=512, act="bf16", expert="bf16",
+                    shared="bf16", out="bf16", bias=None, d=None, layers=48)
+    if name == "ling_verify":
+        return dict(T=T_override or 4, H=2560, E=512, k=8, I=768, I_shared=768, act="bf16", expert="bf16",
+                    shared="bf16", out="bf16", bias="verify", d=d, layers=8)
+    if name == "ling_mxfp4":
+        T = T_override or 1
+        return dict(T=T, H=2560, E=512, k=8, I=768, I_shared=768, act="bf16", expert="mxfp4",
+                    shared="bf16", out="f32", bias=("verify" if T > 1 else None), d=(d if T > 1 else None),
+                    layers=48)
+    if name == "qwen_prefill":
+        return dict(T=T_override or 4096, H=2048, E=256, k=8, I=512, I_shared=512, act="bf16", expert="bf16",
+                    shared="bf16", out="bf16", bias="zipf", d=None, layers=8)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def expert_bytes(spec):
+    """Bytes of one routed expert's gate+up and down weights."""
+    H, I = spec["H"], spec["I"]
+    if spec["expert"] == "mxfp4":
+        gu = 2 * (I * H // 2 + I * H // 32)
+        dn = H * I // 2 + H * I // 32
+    else:
+        es = 4 if spec["expert"] == "f32" else 2
+        gu, dn = 2 * I * H * es, H * I * es
+    return gu, dn
+
+
+def algorithmic_bytes(spec, distinct):
+    """Bytes the layer must move once: the distinct selected experts, the shared expert,
+    the fp32 router, x and y."""
+    H, E, T, Is = spec["H"], spec["E"], spec["T"], spec["I_shared"]
+    gu, dn = expert_bytes(spec)
+    ss = 2 if spec["shared"] == "bf16" else 4
+    shared = 3 * Is * H * ss
+    router = E * H * 4
+    xs = T * H * (2 if spec["act"] == "bf16" else 4)
+    ys = T * H * (2 if spec["out"] == "bf16" else 4)
+    return distinct * (gu + dn) + shared + router + xs + ys
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="qwen_decode")
+    ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--d", type=int, default=32)
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer is built for a single MI355X; "
+              "run it with --gpus 1 (multi-GPU sharding is described, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from routed_expert_ffn_route_amd import binding as B
+    from routed_expert_ffn_route_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()
+    spec = workload_spec(args.workload, args.T, args.d)
+    nl = args.layers or spec["layers"]
+    T = spec["T"]
+    print(f"# generating {nl} layers of {args.workload} on the device", file=sys.stderr, flush=True)
+    layers = []
+    for li in range(nl):
+        Ld, xd = synth.device_layer(T, spec["H"], spec["E"], spec["k"], spec["I"], spec["I_shared"],
+                                    spec["act"], spec["expert"], spec["shared"], spec["out"], seed=li,
+                                    bias=spec["bias"], d=spec["d"])
+        layers.append((Ld, xd, B.weights_of(Ld)))
+    torch.cuda.synchronize()
+    shape = B.shape_of(layers[0][0])
+    path = B.path_name(shape)
+    ws = B.workspace(shape)
+    y = torch.empty((T, spec["H"]), device="cuda",
+                    dtype=torch.float32 if spec["out"] == "f32" else torch.int16)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    # distinct experts per layer (for the bytes model), from the library's own routing
+    distinct = []
+    for Ld, xd, _ in layers:
+        r = B.layer_route(Ld, xd)
+        distinct.append(len(set(r["ids"].cpu().numpy().ravel().tolist())))
+    mean_distinct = float(np.mean(distinct))
+
+    def step(i):
+        Ld, xd, w = layers[i % nl]
+        B.forward(shape, xd, w, y, ws, sp)
+
+    print(f"# path {path}; warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps between events on the launch stream ----
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+
+    # ---- per-kernel durations: the same K steps with every launch bracketed by HIP events
+    B.timing_begin(8 * args.steps)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i)
+    ktimes = B.timing_end()
+    torch.cuda.synchronize()
+    kern = {n: (c, ms / c) for n, (c, ms) in ktimes.items()}
+    dom = max(kern, key=lambda n: kern[n][0] * kern[n][1])
+    dom_ms = kern[dom][1]
+
+    gu, dn = expert_bytes(spec)
+    if dom == "dec_gateup":
+        dom_bytes = mean_distinct * gu
+    elif dom == "dec_down":
+        Is, H = spec["I_shared"], spec["H"]
+        dom_bytes = mean_distinct * dn + Is * H * (2 if spec["shared"] == "bf16" else 4)
+    elif dom == "dec_router_shared":
+        dom_bytes = spec["E"] * spec["H"] * 4 + 2 * spec["I_shared"] * spec["H"] * 2
+    else:
+        dom_bytes = None
+    layer_bytes = algorithmic_bytes(spec, mean_distinct)
+    tok_s = T / (ms_step / 1e3)
+    layer_gbs = layer_bytes / (ms_step / 1e3) / 1e9
+
+    roof = None
+    if dom_bytes is not None:
+        ach = dom_bytes / (dom_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "kernel_us": round(dom_ms * 1e3, 3), "bytes_per_launch": int(dom_bytes)}
+
+    # ---- CPU baseline: the oracle, single-threaded, on a bounded sample of the workload ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        Ld0, _, _ = layers[0]
+        Lh = synth.to_host(Ld0)
+        xs = [synth.to_host(layers[i % nl][0].with_T(T), layers[i % nl][1])[1] for i in range(1)]
+        n, t0 = 0, time.perf_counter()
+        rng = np.random.default_rng(1234)
+        while True:
+            xh = synth.f32_to_bf16_bits(rng.standard_normal((T, spec["H"]), dtype=np.float32)) \
+                if spec["act"] == "bf16" else rng.standard_normal((T, spec["H"]), dtype=np.float32)
+            oracle.forward(Lh, xh)
+            n += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds and n >= 2:
+                break
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(n * T / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} calls of T={T} on layer 0 (fresh x each), {dt:.1f} s, one thread"}
+        del Lh, xs
+
+    out = {
+        "metric": "MoE layer tok/s + HBM GB/s (% of peak) at T=1/T=4 decode; TFLOP/s at prefill",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": spec["expert"], "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "H": spec["H"], "E": spec["E"], "k": spec["k"],
+                   "I": spec["I"], "I_shared": spec["I_shared"], "layers_rotated": nl,
+                   "path": path, "distinct_experts_mean": mean_distinct},
+        "layer_gbs": round(layer_gbs, 1), "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+        "layer_bytes": int(layer_bytes), "us_per_call": round(ms_step * 1e3, 3),
+        "kernels_us": {n: round(v[1] * 1e3, 3) for n, v in kern.items()},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

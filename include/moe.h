@@ -1,0 +1,179 @@
+/*
+ * libmoe -- routed-expert FFN layer (sparse mixture of experts) on MI355X.
+ *
+ * C ABI.  Every array argument is a plain pointer to caller-owned DEVICE
+ * memory (HBM of the current HIP device); every size is in elements unless a
+ * name ends in _bytes.  The library allocates nothing on the device and
+ * never synchronises the host inside a call: calls enqueue kernels on the
+ * given HIP stream and return.
+ *
+ * What the layer computes, per token t (sources are the pages this project
+ * follows; readings taken where they are silent are marked "reading"):
+ *   l[t][e] = sum_h x[t][h] * Wr[e][h] + bias[t][e]                (router)
+ *   S_t     = the k experts with the largest l[t][e]; ties go to the lower
+ *             expert index; listed by descending logit             (reading)
+ *   w[t][j] = softmax_e(l[t])[e_j] / sum_{i<k} softmax_e(l[t])[e_i] (reading)
+ *   FFN_e(v) = Wd_e ( silu(Wg_e v) * (Wu_e v) ),  silu(z) = z/(1+exp(-z))
+ *   y[t]    = sum_j w[t][j] * FFN_{e_j}(x[t]) + FFN_shared(x[t])
+ * "Optimizing on-device inference for Apple Silicon" (Perplexity), sections
+ * "Qwen creates three distinct workload shapes" (a router scores every
+ * routed expert and picks eight; one shared expert sees every token) and
+ * "Reduce intermediate and state traffic" (gate/up projections with a gated
+ * activation; output projection combined with the routing score and the
+ * shared expert's result).  "Three ways to boost mixture-of-experts
+ * inference on NVIDIA DGX Spark", sections "Why decoding was slow in the
+ * first place" and "Optimization 1" (512 experts, top-8, a shared expert,
+ * MXFP4 expert weights).
+ *
+ * Layouts (reading: nn.Linear [out][in], reduction index contiguous):
+ *   x        [T][H]          act_dtype
+ *   router_w [E][H]          fp32
+ *   gate, up [E][I][H]       expert_dtype   (MXFP4: codes [E][I][H/2])
+ *   down     [E][H][I]       expert_dtype   (MXFP4: codes [E][H][I/2])
+ *   MXFP4    two e2m1 codes per byte, element 2i in the low nibble; one e8m0
+ *            scale byte per 32 consecutive elements of a row:
+ *            gate_s, up_s [E][I][H/32], down_s [E][H][I/32]  (OCP MX v1.0)
+ *   sh_gate, sh_up [I_shared][H], sh_down [H][I_shared]   shared_dtype
+ *   y        [T][H]          out_dtype
+ *
+ * Error behaviour: every entry point validates all arguments before it
+ * enqueues anything; on a negative return nothing was launched and no output
+ * was written.  NaN/Inf inputs are not checked; they propagate.
+ */
+#ifndef LIBMOE_MOE_H
+#define LIBMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)        /* null required pointer, bad size, k > E ...   */
+#define MOE_EUNSUPPORTED (-2)  /* dtype combination or shape outside limits    */
+#define MOE_EALIGN (-3)        /* a pointer is not 16-byte aligned             */
+#define MOE_EWORKSPACE (-4)    /* workspace null or smaller than required      */
+#define MOE_EHIP (-5)          /* a HIP runtime call or kernel launch failed   */
+
+/* Element encodings. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype_t;
+
+/* Limits checked by every entry point. */
+#define MOE_MAX_E 1024     /* routed experts                                   */
+#define MOE_MAX_K 16       /* experts per token                                */
+#define MOE_MAX_H 16384    /* hidden size                                      */
+#define MOE_MAX_I 8192     /* intermediate sizes                               */
+
+typedef struct {
+  int32_t T;            /* tokens, >= 1                                        */
+  int32_t H;            /* hidden size, multiple of 32                         */
+  int32_t E;            /* routed experts, 1..MOE_MAX_E                        */
+  int32_t k;            /* experts per token, 1..min(E, MOE_MAX_K)             */
+  int32_t I;            /* routed intermediate size, multiple of 32            */
+  int32_t I_shared;     /* shared intermediate size, multiple of 32; 0 = none  */
+  int32_t act_dtype;    /* x:          MOE_F32 | MOE_BF16                      */
+  int32_t expert_dtype; /* gate/up/down: MOE_F32 | MOE_BF16 | MOE_MXFP4        */
+  int32_t shared_dtype; /* shared expert: MOE_F32 | MOE_BF16                   */
+  int32_t out_dtype;    /* y:          MOE_F32 | MOE_BF16                      */
+} moe_shape_t;
+
+typedef struct {
+  const float *router_w;     /* [E][H], required                               */
+  const float *router_bias;  /* nullable; [E] if bias_t_stride == 0,
+                                [T][E] if bias_t_stride == E                   */
+  int64_t bias_t_stride;
+  const void *gate, *up, *down;          /* required                           */
+  const uint8_t *gate_s, *up_s, *down_s; /* required iff expert_dtype MXFP4    */
+  const void *sh_gate, *sh_up, *sh_down; /* required iff I_shared > 0          */
+} moe_weights_t;
+
+typedef struct {          /* outputs of moe_route; ids and w required         */
+  int32_t *topk_ids;      /* [T][k] chosen experts, descending logit           */
+  float *topk_w;          /* [T][k] combine weights (sum to 1 per token)       */
+  float *logits;          /* nullable; [T][E] biased router logits             */
+  int32_t *expert_count;  /* nullable; [E] assignments per expert (histogram)  */
+  int32_t *expert_offset; /* nullable; [E+1] exclusive prefix scan of counts   */
+  int32_t *sorted_slot;   /* nullable; [T*k] slots s = t*k + j grouped by
+                             expert: group e is sorted_slot[offset[e] ..
+                             offset[e+1]); the order inside a group is not
+                             specified                                         */
+} moe_route_out_t;
+
+/*
+ * Workspace bytes that moe_route / moe_forward need for this shape.  The
+ * caller allocates that many bytes of device memory (256-byte aligned, as
+ * hipMalloc returns), ZERO-FILLS IT ONCE before its first use, and passes it
+ * to every call.  Calls leave the workspace's control words zero again on
+ * return, so it never needs re-zeroing.  One workspace must not be used by
+ * two calls that may run concurrently (e.g. on two streams).
+ * Returns MOE_OK, MOE_EINVAL (null pointer) or a shape-validation error.
+ */
+int moe_workspace_size(const moe_shape_t *shape, size_t *bytes);
+
+/*
+ * Routing only: router logits, top-k selection, combine weights, and the
+ * token-to-expert permutation (histogram of assignments per expert, prefix
+ * scan to start offsets, scatter of slots into expert groups) --
+ * "Optimizing on-device inference for Apple Silicon", section "Keep expert
+ * routing on the GPU".
+ *   x          [T][H] act_dtype; ignored when logits_in is given
+ *   logits_in  nullable [T][E] fp32: if given, selection runs on these
+ *              logits (bias is NOT added again) instead of the router
+ *   out        output pointers, see moe_route_out_t
+ *   ws         workspace of ws_bytes >= moe_workspace_size()
+ *   stream     hipStream_t (NULL = default stream)
+ * Only gate/up/down-independent fields of `w` are read (router_w, bias).
+ */
+int moe_route(const moe_shape_t *shape, const void *x, const moe_weights_t *w,
+              const float *logits_in, const moe_route_out_t *out, void *ws,
+              size_t ws_bytes, void *stream);
+
+/*
+ * The whole layer: y = routed experts combined with their weights + shared
+ * expert, for all T tokens.  No host synchronisation, no allocation; the
+ * launch configuration depends on the shape only, so the call can be
+ * captured into a HIP graph.  y must not alias x, the weights or ws.
+ *   x [T][H] act_dtype, y [T][H] out_dtype, ws/ws_bytes as above,
+ *   stream hipStream_t (NULL = default stream).
+ */
+int moe_forward(const moe_shape_t *shape, const void *x, const moe_weights_t *w,
+                void *y, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Name of the kernel path moe_forward takes for this shape, e.g.
+ * "decode.bf16" or "prefill.bf16" ("Three ways to boost mixture-of-experts
+ * inference on NVIDIA DGX Spark", section "What this means for your
+ * deployment": check at start-up that the intended path is the active one).
+ * Returns "invalid" for a shape that fails validation.  Static string.
+ */
+const char *moe_path_name(const moe_shape_t *shape);
+
+/* Static text for a return code. */
+const char *moe_strerror(int code);
+
+/*
+ * Kernel timing for measurement.  moe_timing_begin(n) creates n pairs of
+ * HIP events (an allocation: call it outside any timed or captured region);
+ * afterwards every kernel that moe_forward launches is bracketed by an event
+ * pair on the call's stream until the pairs run out.  moe_timing_end()
+ * synchronises those events, writes for each distinct kernel its name, the
+ * number of timed launches and their summed duration in milliseconds
+ * (up to max_out entries, *n_out set to the count), destroys the events and
+ * turns timing off.  Not thread-safe; for benchmarks only.
+ */
+typedef struct {
+  char name[64];
+  int32_t launches;
+  double total_ms;
+} moe_kernel_time_t;
+
+int moe_timing_begin(int32_t max_launches);
+int moe_timing_end(moe_kernel_time_t *out, int32_t max_out, int32_t *n_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,12 +1,9 @@
-"""MI355X (gfx950) routed-expert FFN layer: Python binding of libmoe.so.
+"""MI355X (gfx950) routed-expert FFN layer.
 
-The binding is loaded on first use so that ``routed_expert_ffn_route_amd.synth``
-(the seeded input generators) imports without a GPU library present.
+* ``binding`` -- ctypes binding of libmoe.so (include/moe.h): moe_route, moe_forward, ...
+* ``synth``   -- seeded synthetic layers and inputs.
+* ``build``   -- compiles libmoe.so with hipcc.
+
+Submodules are imported explicitly (``from routed_expert_ffn_route_amd import binding``);
+importing the package itself loads no GPU library.
 """
-
-
-def __getattr__(name):
-    if name in ("moe", "binding"):
-        from . import binding
-        return binding
-    raise AttributeError(name)

@@ -1,0 +1,155 @@
+// Device helpers and the argument block shared by the libmoe kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;           // CDNA wavefront width
+constexpr int kDecodeMaxT = 16;     // T at or below this takes the decode (GEMV) path
+
+// ---------------------------------------------------------------------------------------
+// Argument block for every kernel of one call.  Passed by value (kernarg segment).
+// ---------------------------------------------------------------------------------------
+struct Args {
+  int T, H, E, k, I, Is;
+  int act, wdt, sdt, odt;             // moe_dtype_t of x, experts, shared, y
+  const void* x;
+  const float* rw;
+  const float* rbias;
+  long long bias_stride;
+  const void *gate, *up, *down;
+  const uint8_t *gs, *us, *ds;
+  const void *sgate, *sup, *sdown;
+  void* y;
+  // route-only inputs/outputs (moe_route); null in moe_forward
+  const float* logits_in;
+  int* o_ids;
+  float* o_w;
+  float* o_logits;
+  int* o_count;
+  int* o_offset;
+  int* o_sorted;
+  // workspace sections
+  unsigned* ctr;        // control words (kept zero between calls)
+  float* logits;        // [T][E]
+  int* ids;             // [T][k]
+  float* cw;            // [T][k]
+  int* plan;            // decode plan, see DecodePlan
+  float* a_sh;          // [T][Is]   decode: shared-expert activations (fp32)
+  float* a;             // [T*k][I]  decode: routed activations (fp32)
+  // prefill sections
+  int* pf_count;        // [E+1]   (index E = shared expert group)
+  int* pf_offset;       // [E+2]
+  int* pf_rows;         // [T*k + T]   grouped rows: slot ids (shared group: T*k + t)
+  int* pf_tiles;        // tile map entries
+  uint16_t* pf_act;     // [T*k + T][max(I,Is)] bf16 gate/up activations
+  uint16_t* pf_out;     // [T*k + T][H]  bf16 per-row expert outputs (weighted)
+  int router_blocks;    // decode stage-1 grid split
+  int shared_blocks;
+  int tiles_cap;        // capacity of pf_tiles
+};
+
+// Decode plan, written by the router's last block and read by the expert kernels:
+//  * the distinct experts of the T*k assignments in ascending expert id (nd of them), the
+//    tokens using each (bitmask), and per (distinct, token) the slot s = t*k + j and the
+//    combine weight -- drives the gate/up kernel, which streams each distinct expert once;
+//  * the T*k slots ordered by (expert, token) with their expert, token and weight --
+//    drives the down/combine kernel.
+// Layout (ints): nd, pad[63], dexp[D], dmask[D], dslot[D][T], dw[D][T],
+//                sl_exp[S], sl_tok[S], sl_slot[S], sl_w[S]     with D = min(T*k, E), S = T*k.
+struct DecodePlan {
+  int* base;
+  int D, T, S;
+  __host__ __device__ DecodePlan(int* b, int D_, int T_, int S_) : base(b), D(D_), T(T_), S(S_) {}
+  __host__ __device__ int* nd() const { return base; }
+  __host__ __device__ int* dexp() const { return base + 64; }
+  __host__ __device__ unsigned* dmask() const { return (unsigned*)(base + 64 + D); }
+  __host__ __device__ int* dslot() const { return base + 64 + 2 * D; }
+  __host__ __device__ float* dw() const { return (float*)(base + 64 + 2 * D + D * T); }
+  __host__ __device__ int* sl_exp() const { return base + 64 + 2 * D + 2 * D * T; }
+  __host__ __device__ int* sl_tok() const { return sl_exp() + S; }
+  __host__ __device__ int* sl_slot() const { return sl_exp() + 2 * S; }
+  __host__ __device__ float* sl_w() const { return (float*)(sl_exp() + 3 * S); }
+  __host__ __device__ static size_t bytes(int D, int T, int S) {
+    return sizeof(int) * (64 + 2 * (size_t)D + 2 * (size_t)D * T + 4 * (size_t)S);
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Scalar conversions
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// e8m0 scale byte -> fp32 power of two (0xFF -> NaN, 0x00 -> 2^-127 subnormal).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  if (s == 0xffu) return __uint_as_float(0x7fc00000u);
+  if (s == 0u) return __uint_as_float(0x00400000u);
+  return __uint_as_float(s << 23);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Two e2m1 codes in byte `sel` of v -> two bf16 values (exact; unit scale).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t v) {
+  bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, SEL);
+  return __builtin_bit_cast(uint32_t, r);
+}
+// Two e2m1 codes in byte `sel` of v -> two fp32 values (exact; unit scale).
+template <int SEL>
+__device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, SEL);
+}
+
+// ---------------------------------------------------------------------------------------
+// Wave / lane-group reductions (xor butterflies: every lane of the group gets the result)
+// ---------------------------------------------------------------------------------------
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *(const uint4*)p; }
+__device__ __forceinline__ uint2 ldg8(const void* p) { return *(const uint2*)p; }
+__device__ __forceinline__ uint32_t ldg4(const void* p) { return *(const uint32_t*)p; }
+__device__ __forceinline__ float4 ldf4(const float* p) { return *(const float4*)p; }
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Nontemporal 16-byte load for weight streams that are read exactly once per call.
+__device__ __forceinline__ uint4 ldnt16(const void* p) {
+  u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+}  // namespace moe

@@ -1,0 +1,38 @@
+// Host-side launchers of the libmoe kernels (one per path) and the per-launch timing hook.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace moe {
+
+// Called around every kernel launch; the API layer records HIP events here when kernel
+// timing is on (moe_timing_begin), and does nothing otherwise.
+struct LaunchHook {
+  void (*pre_fn)(const char* name, hipStream_t st) = nullptr;
+  void (*post_fn)(hipStream_t st) = nullptr;
+  void pre(const char* name, hipStream_t st) const {
+    if (pre_fn) pre_fn(name, st);
+  }
+  void post(hipStream_t st) const {
+    if (post_fn) post_fn(st);
+  }
+};
+
+// Decode path (T <= kDecodeMaxT): stage 1 (router + shared gate/up + selection/plan),
+// routed gate/up, down + combine.  route_only stops after stage 1.
+int launch_decode(Args A, hipStream_t st, bool route_only, const LaunchHook& hook);
+
+// Routing for any T: router logits (or logits_in), per-token selection, and the
+// histogram / scan / scatter plan written to the moe_route outputs.
+int launch_route_any(Args A, hipStream_t st, bool decode_sized, const LaunchHook& hook);
+
+// Prefill path (T > kDecodeMaxT): grouped GEMMs on MFMA.
+int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook);
+
+// Workspace bytes needed by the prefill path's sections (0 for decode-sized T).
+size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is);
+int prefill_tiles_cap(int T, int E, int k);
+
+}  // namespace moe

@@ -206,7 +206,7 @@ def device_layer(T, H, E, k, I, I_shared, act=BF16, expert=BF16, shared=BF16, ou
             a.mul_(std)
         if dt == F32:
             return a
-        return a.to(torch.bfloat16).view(torch.uint16)
+        return a.to(torch.bfloat16).view(torch.int16)
 
     x = normal((T, H), 1.0, act)
     router_w = normal((E, H), 1.0 / math.sqrt(H), F32)
@@ -226,7 +226,7 @@ def device_layer(T, H, E, k, I, I_shared, act=BF16, expert=BF16, shared=BF16, ou
         L.up, L.up_s = codes((E, I, H // 2)), scales((E, I, H // 32))
         L.down, L.down_s = codes((E, H, I // 2)), scales((E, H, I // 32))
     else:
-        L.gate = torch.empty((E, I, H), device=device, dtype=torch.float32 if expert == F32 else torch.uint16)
+        L.gate = torch.empty((E, I, H), device=device, dtype=torch.float32 if expert == F32 else torch.int16)
         L.up = torch.empty_like(L.gate)
         L.down = torch.empty((E, H, I), device=device, dtype=L.gate.dtype)
         for e in range(E):
@@ -247,7 +247,10 @@ def to_device(L: Layer, x, device="cuda"):
         if a is None:
             return None
         if isinstance(a, np.ndarray):
-            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:   # bf16 bit patterns travel as int16 on the device
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to(device)
         return a.to(device)
     D = dataclasses.replace(L, **{f: mv(a) for f, a in L.arrays()})
     return D, mv(x)
@@ -257,6 +260,7 @@ def to_host(L: Layer, x=None):
     def mv(a):
         if a is None or isinstance(a, np.ndarray):
             return a
-        return a.detach().cpu().numpy()
+        h = a.detach().cpu().numpy()
+        return h.view(np.uint16) if h.dtype == np.int16 else h
     H = dataclasses.replace(L, **{f: mv(a) for f, a in L.arrays()})
     return (H, mv(x)) if x is not None else H
