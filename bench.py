@@ -81,6 +81,7 @@ def main():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -122,32 +123,46 @@ def main():
         distinct.append(len(set(r["ids"].cpu().numpy().ravel().tolist())))
     mean_distinct = float(np.mean(distinct))
 
-    def step(i):
+    def step(i, sp):
         Ld, xd, w = layers[i % nl]
         B.forward(shape, xd, w, y, ws, sp)
 
     print(f"# path {path}; warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        step(i)
+        step(i, stream.cuda_stream)
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps between events on the launch stream ----
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
+    def timed(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(torch.cuda.current_stream())
+        fn()
+        e1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    # ---- eager: K back-to-back calls on the stream ----
+    ms_eager = timed(lambda: [step(i, stream.cuda_stream) for i in range(args.steps)])
+
+    # ---- graph: the same K calls captured once into a HIP graph and replayed ----
+    ms_graph = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=cs):
+            for i in range(args.steps):
+                step(i, cs.cuda_stream)
+        g.replay()  # untimed
+        torch.cuda.synchronize()
+        ms_graph = timed(g.replay)
+    ms_step = ms_graph if ms_graph is not None else ms_eager
 
     # ---- per-kernel durations: the same K steps with every launch bracketed by HIP events
     B.timing_begin(8 * args.steps)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(i)
+        step(i, stream.cuda_stream)
     ktimes = B.timing_end()
     torch.cuda.synchronize()
     kern = {n: (c, ms / c) for n, (c, ms) in ktimes.items()}
@@ -204,6 +219,8 @@ def main():
         "config": {"workload": args.workload, "T": T, "H": spec["H"], "E": spec["E"], "k": spec["k"],
                    "I": spec["I"], "I_shared": spec["I_shared"], "layers_rotated": nl,
                    "path": path, "distinct_experts_mean": mean_distinct},
+        "launch": "hipgraph" if ms_graph is not None else "eager",
+        "us_per_call_eager": round(ms_eager * 1e3, 3),
         "layer_gbs": round(layer_gbs, 1), "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
         "layer_bytes": int(layer_bytes), "us_per_call": round(ms_step * 1e3, 3),
         "kernels_us": {n: round(v[1] * 1e3, 3) for n, v in kern.items()},

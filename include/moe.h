@@ -103,12 +103,11 @@ typedef struct {          /* outputs of moe_route; ids and w required         */
 } moe_route_out_t;
 
 /*
- * Workspace bytes that moe_route / moe_forward need for this shape.  The
- * caller allocates that many bytes of device memory (256-byte aligned, as
- * hipMalloc returns), ZERO-FILLS IT ONCE before its first use, and passes it
- * to every call.  Calls leave the workspace's control words zero again on
- * return, so it never needs re-zeroing.  One workspace must not be used by
- * two calls that may run concurrently (e.g. on two streams).
+ * Workspace bytes that moe_route / moe_forward need for this shape.  The caller
+ * allocates that many bytes of device memory (16-byte aligned; hipMalloc's 256-byte
+ * alignment is fine) and passes it to every call.  Its contents need no initialisation
+ * and carry nothing from one call to the next.  One workspace must not be used by two
+ * calls that may run concurrently (e.g. on two streams).
  * Returns MOE_OK, MOE_EINVAL (null pointer) or a shape-validation error.
  */
 int moe_workspace_size(const moe_shape_t *shape, size_t *bytes);

@@ -41,7 +41,7 @@ int check_shape(const moe_shape_t* s) {
 }
 
 struct Layout {
-  size_t ctr, logits, ids, cw, plan, a_sh, a, pf, total;
+  size_t logits, ids, cw, plan, a_sh, a, pf, total;
 };
 
 Layout layout(const moe_shape_t* s) {
@@ -49,8 +49,6 @@ Layout layout(const moe_shape_t* s) {
   const size_t T = s->T, E = s->E, k = s->k, S = T * k;
   const size_t D = S < E ? S : E;
   size_t off = 0;
-  L.ctr = off;
-  off += up(256);
   L.logits = off;
   off += up(T * E * 4);
   L.ids = off;
@@ -100,7 +98,6 @@ Args make_args(const moe_shape_t* s, const void* x, const moe_weights_t* w, void
   A.sdown = w->sh_down;
   const Layout L = layout(s);
   uint8_t* b = (uint8_t*)ws;
-  A.ctr = (unsigned*)(b + L.ctr);
   A.logits = (float*)(b + L.logits);
   A.ids = (int*)(b + L.ids);
   A.cw = (float*)(b + L.cw);

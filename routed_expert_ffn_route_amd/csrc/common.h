@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 namespace moe {
 
@@ -34,7 +34,6 @@ struct Args {
   int* o_offset;
   int* o_sorted;
   // workspace sections
-  unsigned* ctr;        // control words (kept zero between calls)
   float* logits;        // [T][E]
   int* ids;             // [T][k]
   float* cw;            // [T][k]
@@ -122,19 +121,50 @@ __device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Wave / lane-group reductions (xor butterflies: every lane of the group gets the result)
+// Wave / lane-group reductions.  Within a 16-lane row the butterfly runs on DPP lane
+// permutes (xor 1, xor 2 by quad_perm, xor 4 by row_half_mirror, xor 8 by row_mirror),
+// which cost no LDS traffic; the 16-lane row results are combined with readlane.  Every
+// lane of a group gets the group's result.
 // ---------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+constexpr int kDppXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+__device__ __forceinline__ float rl(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "G");
+  if constexpr (G >= 2) v += dpp_f<kDppXor1>(v);
+  if constexpr (G >= 4) v += dpp_f<kDppXor2>(v);
+  if constexpr (G >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (G >= 16) v += dpp_f<kDppMirror>(v);
+  if constexpr (G == 32) {
+    const float a = rl(v, 0) + rl(v, 16), b = rl(v, 32) + rl(v, 48);
+    v = ((int)__lane_id() < 32) ? a : b;
+  } else if constexpr (G == 64) {
+    v = (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
+  }
   return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return fmaxf(fmaxf(rl(v, 0), rl(v, 16)), fmaxf(rl(v, 32), rl(v, 48)));
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }

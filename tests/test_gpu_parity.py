@@ -274,7 +274,7 @@ def test_mxfp4_small_shapes(orc, B):
 
 def test_deterministic_and_workspace_reuse(orc, B):
     """Same inputs twice give identical bits; one workspace serves calls of different
-    inputs back to back (its control words are left zero after every call)."""
+    inputs back to back, and needs no initialisation (here: filled with garbage)."""
     import torch
     say("[determinism]")
     La, xa = synth.make_layer(4, 512, 64, 8, 128, 128, seed=21)
@@ -282,11 +282,11 @@ def test_deterministic_and_workspace_reuse(orc, B):
     Lda, xda = synth.to_device(La, xa)
     Ldb, xdb = synth.to_device(Lb, xb)
     ws = B.workspace(B.shape_of(Lda))
+    ws.fill_(0xA5)
     ya1 = B.layer_forward(Lda, xda, ws=ws).clone()
     yb = B.layer_forward(Ldb, xdb, ws=ws).clone()
     ya2 = B.layer_forward(Lda, xda, ws=ws).clone()
     torch.cuda.synchronize()
     assert torch.equal(ya1.view(torch.int16), ya2.view(torch.int16))
-    assert int(ws[:4].view(torch.int32)[0]) == 0
     ref_b = orc.forward(Lb, xb)[0]
     check_out(Lb, y_host(Lb, yb), ref_b, "ws-reuse")
