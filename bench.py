@@ -70,6 +70,21 @@ def algorithmic_bytes(spec, distinct):
     return distinct * (gu + dn) + shared + router + xs + ys
 
 
+def traffic_from_profiles(kernel, workload, T):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel's source changed since the counters were taken."""
+    from routed_expert_ffn_route_amd import profsum
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_T{T}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("TRAFFIC_JSON:"):
+            d = json.loads(line.split(":", 1)[1])
+            if d.get("source_hash") == profsum.source_hash(kernel):
+                return d["traffic_bytes"]
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +97,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -170,46 +187,64 @@ def main():
     dom_ms = kern[dom][1]
 
     gu, dn = expert_bytes(spec)
-    if dom == "dec_gateup":
-        dom_bytes = mean_distinct * gu
-    elif dom == "dec_down":
-        Is, H = spec["I_shared"], spec["H"]
-        dom_bytes = mean_distinct * dn + Is * H * (2 if spec["shared"] == "bf16" else 4)
-    elif dom == "dec_router_shared":
-        dom_bytes = spec["E"] * spec["H"] * 4 + 2 * spec["I_shared"] * spec["H"] * 2
-    else:
-        dom_bytes = None
+    H, I, Is, E, k = spec["H"], spec["I"], spec["I_shared"], spec["E"], spec["k"]
+    ss = 2 if spec["shared"] == "bf16" else 4
     layer_bytes = algorithmic_bytes(spec, mean_distinct)
     tok_s = T / (ms_step / 1e3)
     layer_gbs = layer_bytes / (ms_step / 1e3) / 1e9
-
+    # algorithmic work of one launch of each kernel: bytes for the HBM-bound decode kernels,
+    # flops for the prefill GEMMs
+    work = {
+        "dec_router_shared": ("hbm", E * H * 4 + 2 * Is * H * ss),
+        "dec_gateup": ("hbm", mean_distinct * gu),
+        "dec_down": ("hbm", mean_distinct * dn + Is * H * ss),
+        "pf_gateup": ("mfma", 2.0 * 2 * (T * k * I + T * Is) * H),
+        "pf_down": ("mfma", 2.0 * (T * k * I + T * Is) * H),
+        "pf_router": ("mfma", 2.0 * 3 * T * E * H),
+    }
     roof = None
-    if dom_bytes is not None:
-        ach = dom_bytes / (dom_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
-                "kernel_us": round(dom_ms * 1e3, 3), "bytes_per_launch": int(dom_bytes)}
+    if dom in work:
+        bound, amount = work[dom]
+        if bound == "hbm":
+            ach, peak, unit = amount / (dom_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
+        else:
+            ach, peak, unit = amount / (dom_ms / 1e3) / 1e12, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
+        roof = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "traffic": traffic_from_profiles(dom, args.workload, T),
+                "kernel": dom, "kernel_us": round(dom_ms * 1e3, 3),
+                ("bytes_per_launch" if bound == "hbm" else "flops_per_launch"): int(amount)}
 
     # ---- CPU baseline: the oracle, single-threaded, on a bounded sample of the workload ----
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        Ld0, _, _ = layers[0]
-        Lh = synth.to_host(Ld0)
-        xs = [synth.to_host(layers[i % nl][0].with_T(T), layers[i % nl][1])[1] for i in range(1)]
+        Lh = synth.to_host(layers[0][0])
+        Ts = min(T, 4)  # tokens are independent: the oracle runs a few at a time
+        Lh = Lh.with_T(Ts)
+        if Lh.router_bias is not None and Lh.bias_t_stride:
+            Lh.router_bias = np.ascontiguousarray(Lh.router_bias[:Ts])
         n, t0 = 0, time.perf_counter()
         rng = np.random.default_rng(1234)
         while True:
-            xh = synth.f32_to_bf16_bits(rng.standard_normal((T, spec["H"]), dtype=np.float32)) \
-                if spec["act"] == "bf16" else rng.standard_normal((T, spec["H"]), dtype=np.float32)
+            xr = rng.standard_normal((Ts, spec["H"]), dtype=np.float32)
+            xh = synth.f32_to_bf16_bits(xr) if spec["act"] == "bf16" else xr
             oracle.forward(Lh, xh)
             n += 1
             if time.perf_counter() - t0 >= args.cpu_seconds and n >= 2:
                 break
         dt = time.perf_counter() - t0
-        cpu = {"value": round(n * T / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n} calls of T={T} on layer 0 (fresh x each), {dt:.1f} s, one thread"}
-        del Lh, xs
+        cpu = {"value": round(n * Ts / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} oracle calls of {Ts} token(s) each on layer 0 of the workload "
+                         f"(fresh seeded x per call), {dt:.1f} s on one host thread"}
+        del Lh
+
+    if args.copy_calibration:
+        a = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     out = {
         "metric": "MoE layer tok/s + HBM GB/s (% of peak) at T=1/T=4 decode; TFLOP/s at prefill",

@@ -28,6 +28,9 @@ int launch_decode(Args A, hipStream_t st, bool route_only, const LaunchHook& hoo
 // histogram / scan / scatter plan written to the moe_route outputs.
 int launch_route_any(Args A, hipStream_t st, bool decode_sized, const LaunchHook& hook);
 
+// Router (MFMA, bf16 activations) + selection for T > kDecodeMaxT.
+int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook);
+
 // Prefill path (T > kDecodeMaxT): grouped GEMMs on MFMA.
 int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook);
 

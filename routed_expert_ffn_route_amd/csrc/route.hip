@@ -177,25 +177,27 @@ __global__ __launch_bounds__(1024) void permute(const int* ids, int T, int k, in
 
 int launch_route_any(Args A, hipStream_t st, bool decode_sized, const LaunchHook& hook) {
   hipError_t err;
-  if (decode_sized) {  // the decode path's router kernel (no shared-expert blocks)
+  if (!decode_sized && A.act == MOE_BF16) {  // the prefill path's router and selection
+    const int rc = launch_pf_route(A, st, hook);
+    if (rc) return rc;
+  } else {
     if (!A.logits_in) {
-      int rc = launch_decode(A, st, /*route_only=*/true, hook);
-      if (rc) return rc;
+      if (decode_sized) {  // the decode path's router kernel (no shared-expert blocks)
+        const int rc = launch_decode(A, st, /*route_only=*/true, hook);
+        if (rc) return rc;
+      } else {
+        dim3 grid((A.T + 63) / 64, (A.E + 63) / 64);
+        hook.pre("route_logits", st);
+        router_tiled<MOE_F32><<<grid, 256, 0, st>>>(A);
+        hook.post(st);
+        if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
+      }
     }
-  } else if (!A.logits_in) {
-    dim3 grid((A.T + 63) / 64, (A.E + 63) / 64);
-    hook.pre("route_logits", st);
-    if (A.act == MOE_F32)
-      router_tiled<MOE_F32><<<grid, 256, 0, st>>>(A);
-    else
-      router_tiled<MOE_BF16><<<grid, 256, 0, st>>>(A);
+    hook.pre("route_select", st);
+    select_tokens<<<(A.T + 3) / 4, 256, 0, st>>>(A);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   }
-  hook.pre("route_select", st);
-  select_tokens<<<(A.T + 3) / 4, 256, 0, st>>>(A);
-  hook.post(st);
-  if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   if (A.o_count || A.o_offset || A.o_sorted) {
     hook.pre("route_permute", st);
     permute<<<1, 1024, 0, st>>>(A.ids, A.T, A.k, A.E, false, A.o_count, A.o_offset, A.o_sorted,

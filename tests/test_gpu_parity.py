@@ -290,3 +290,56 @@ def test_deterministic_and_workspace_reuse(orc, B):
     assert torch.equal(ya1.view(torch.int16), ya2.view(torch.int16))
     ref_b = orc.forward(Lb, xb)[0]
     check_out(Lb, y_host(Lb, yb), ref_b, "ws-reuse")
+
+
+# ---- prefill path (T > 16): grouped MFMA GEMMs ------------------------------------------
+
+@pytest.mark.parametrize("kw", [
+    dict(T=17, H=256, E=16, k=2, I=128, I_shared=128),           # smallest prefill batch
+    dict(T=64, H=512, E=32, k=4, I=192, I_shared=64, bias="zipf"),  # ragged tiles, skewed load
+    dict(T=300, H=1024, E=64, k=8, I=512, I_shared=512, bias="zipf"),
+    dict(T=200, H=96, E=8, k=2, I=96, I_shared=0),               # K not a multiple of 64, no shared
+    dict(T=129, H=2048, E=256, k=8, I=512, I_shared=512),        # Qwen shapes, one row past a tile
+])
+def test_prefill_small_bf16(orc, B, kw):
+    say(f"[prefill] {kw}")
+    Lh, xh = synth.make_layer(**kw, seed=7)
+    Ld, xd = synth.to_device(Lh, xh)
+    assert B.path_name(B.shape_of(Ld)) == "prefill.bf16"
+    full_check(orc, B, Lh, xh, Ld, xd, f"prefill {kw}")
+
+
+def test_prefill_f32_out(orc, B):
+    say("[prefill-f32out]")
+    Lh, xh = synth.make_layer(40, 256, 16, 4, 64, 64, out="f32", seed=8)
+    Ld, xd = synth.to_device(Lh, xh)
+    full_check(orc, B, Lh, xh, Ld, xd, "prefill f32out")
+
+
+def test_qwen_prefill_full_size_sampled(orc, B):
+    """Qwen-shaped prefill (T=4096, 256 experts top-8, Zipf(1.1) expert bias, bf16) at full
+    size in the benchmark's launch configuration; the oracle checks a sample of tokens one by
+    one (tokens are independent), including tokens of the most loaded expert."""
+    import torch
+    say("[qwen-prefill] T=4096")
+    Ld, xd = synth.device_layer(4096, 2048, 256, 8, 512, 512, seed=0, bias="zipf")
+    y = y_host(Ld, forward_dev(B, Ld, xd))
+    r = B.layer_route(Ld, xd)
+    torch.cuda.synchronize()
+    gids = r["ids"].cpu().numpy()
+    counts = r["count"].cpu().numpy()
+    say(f"  max tokens/expert {counts.max()}, idle experts {(counts == 0).sum()}")
+    assert counts.sum() == 4096 * 8
+    hot = int(np.argmax(counts))
+    rng = np.random.default_rng(0)
+    pick = sorted(set(rng.choice(4096, 40, replace=False).tolist()) |
+                  set(np.nonzero((gids == hot).any(axis=1))[0][:12].tolist()) | {0, 4095})
+    Lh, xh = host_view_for_oracle(Ld, xd)
+    sub = Lh.with_T(len(pick))
+    xs = np.ascontiguousarray(xh[pick])
+    lg, ids, w = oracle_routing(orc, sub, xs)
+    diff = check_routing(orc, sub, xs, gids[pick], lg, ids, "prefill-4096")
+    ref = orc.forward_with_routing(sub, xs, ids, w)
+    keep = [i for i in range(len(pick)) if i not in diff]
+    check_out(sub, y[pick][keep], ref[keep], "prefill-4096 sampled")
+    assert np.all(np.isfinite(y))
