@@ -40,6 +40,7 @@ struct Args {
   int* plan;            // decode plan, see DecodePlan
   float* a_sh;          // [T][Is]   decode: shared-expert activations (fp32)
   float* a;             // [T*k][I]  decode: routed activations (fp32)
+  float* y_sh;          // [T][H]    decode: shared-expert output (fp32)
   // prefill sections
   int* pf_count;        // [E+1]   (index E = shared expert group)
   int* pf_offset;       // [E+2]
@@ -52,29 +53,23 @@ struct Args {
   int tiles_cap;        // capacity of pf_tiles
 };
 
-// Decode plan, written by the router's last block and read by the expert kernels:
-//  * the distinct experts of the T*k assignments in ascending expert id (nd of them), the
-//    tokens using each (bitmask), and per (distinct, token) the slot s = t*k + j and the
-//    combine weight -- drives the gate/up kernel, which streams each distinct expert once;
-//  * the T*k slots ordered by (expert, token) with their expert, token and weight --
-//    drives the down/combine kernel.
-// Layout (ints): nd, pad[63], dexp[D], dmask[D], dslot[D][T], dw[D][T],
-//                sl_exp[S], sl_tok[S], sl_slot[S], sl_w[S]     with D = min(T*k, E), S = T*k.
+// Decode plan, written by the selection kernel and read by both expert kernels: the
+// distinct experts of the T*k assignments in ascending expert id (nd of them), the tokens
+// routed to each (bitmask), and per (distinct expert, token) the slot s = t*k + j that holds
+// that token's activations and its combine weight (slot 0 and weight 0 where the token does
+// not use the expert).  Every distinct expert's weights are then streamed exactly once.
+// Layout (4-byte words): nd, pad[63], dexp[D], dmask[D], dslot[D][T], dw[D][T], D = min(T*k, E).
 struct DecodePlan {
   int* base;
-  int D, T, S;
-  __host__ __device__ DecodePlan(int* b, int D_, int T_, int S_) : base(b), D(D_), T(T_), S(S_) {}
+  int D, T;
+  __host__ __device__ DecodePlan(int* b, int D_, int T_) : base(b), D(D_), T(T_) {}
   __host__ __device__ int* nd() const { return base; }
   __host__ __device__ int* dexp() const { return base + 64; }
   __host__ __device__ unsigned* dmask() const { return (unsigned*)(base + 64 + D); }
   __host__ __device__ int* dslot() const { return base + 64 + 2 * D; }
   __host__ __device__ float* dw() const { return (float*)(base + 64 + 2 * D + D * T); }
-  __host__ __device__ int* sl_exp() const { return base + 64 + 2 * D + 2 * D * T; }
-  __host__ __device__ int* sl_tok() const { return sl_exp() + S; }
-  __host__ __device__ int* sl_slot() const { return sl_exp() + 2 * S; }
-  __host__ __device__ float* sl_w() const { return (float*)(sl_exp() + 3 * S); }
-  __host__ __device__ static size_t bytes(int D, int T, int S) {
-    return sizeof(int) * (64 + 2 * (size_t)D + 2 * (size_t)D * T + 4 * (size_t)S);
+  __host__ __device__ static size_t bytes(int D, int T) {
+    return sizeof(int) * (64 + 2 * (size_t)D + 2 * (size_t)D * T);
   }
 };
 
@@ -93,11 +88,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// e8m0 scale byte -> fp32 power of two (0xFF -> NaN, 0x00 -> 2^-127 subnormal).
+// e8m0 scale byte -> fp32 power of two (0xFF -> NaN, 0x00 -> 2^-127 subnormal).  Branch
+// free, so that a scale still in flight does not hold up the loads issued after it.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  if (s == 0xffu) return __uint_as_float(0x7fc00000u);
-  if (s == 0u) return __uint_as_float(0x00400000u);
-  return __uint_as_float(s << 23);
+  uint32_t b = s << 23;
+  b = s == 0u ? 0x00400000u : b;
+  b = s == 0xffu ? 0x7fc00000u : b;
+  return __uint_as_float(b);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

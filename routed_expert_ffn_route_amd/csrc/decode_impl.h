@@ -1,21 +1,21 @@
-// Decode path (T <= 16): the layer as three bandwidth-bound kernels with no cross-block
-// synchronisation inside any of them.
+// Decode path (T <= 16): the layer as four kernels with no cross-block synchronisation
+// inside any of them (a kernel boundary is the cheapest device-wide barrier).
 //
 //  stage 1  router GEMV (fp32 router rows x all T tokens, one wave per expert row) in some
 //           blocks; the shared expert's gate/up GEMV + SwiGLU in the others -- it needs no
 //           routing, so it runs beside the router ("Optimizing on-device inference for Apple
 //           Silicon", section "Overlap independent GPU work").
-//  gate/up  every block first re-derives the (tiny) selection of all T tokens from the logits,
-//           one wave per token, then takes one (token, rank) slot: the block owning the first
-//           occurrence of an expert streams that expert's gate and up rows once with 16-byte
-//           loads, dots them with every token routed to it and applies SwiGLU in registers
-//           (same page, sections "Optimize the one-row weight path" and "Reduce intermediate
-//           and state traffic"; a window of several tokens touching up to 32 experts is
-//           "Three ways to boost mixture-of-experts inference on NVIDIA DGX Spark", section
-//           "Optimization 3").  Block 0 publishes ids and weights for the next kernel.
-//  down     one lane group per output row h: y[t][h] = sum over t's k slots of
-//           w * (Wd[e][h] . a_slot) + Wd_s[h] . a_s[t]; the block's waves split the slots and
-//           reduce through LDS in a fixed order, so results are deterministic.
+//  select   one block: top-k + renormalised softmax per token (one wave each), then the
+//           distinct experts of the window with their tokens, slots and weights (the plan).
+//           A window of several tokens touches up to T*k experts ("Three ways to boost
+//           mixture-of-experts inference on NVIDIA DGX Spark", section "Optimization 3").
+//  gate/up  block (distinct expert, row tile): streams the expert's gate and up rows once
+//           with 16-byte loads, dots them with every token routed to it and applies SwiGLU
+//           in registers (Apple Silicon page, sections "Optimize the one-row weight path" and
+//           "Reduce intermediate and state traffic").
+//  down     one lane group per output row h: y[t][h] = sum over t's experts of
+//           w * (Wd[e][h] . a) + Wd_s[h] . a_s[t]; the block's waves split the distinct
+//           experts and reduce through LDS in a fixed order, so results are deterministic.
 #pragma once
 
 #include "common.h"
@@ -40,82 +40,135 @@ template <int XT> struct XS;
 template <> struct XS<MOE_F32> { static constexpr int BYTES = 4; };
 template <> struct XS<MOE_BF16> { static constexpr int BYTES = 2; };
 
-template <int WT, int XT>
-__device__ __forceinline__ float chunk_dot(uint4 w, const uint8_t* xrow, int c);
-
-template <>
-__device__ __forceinline__ float chunk_dot<MOE_BF16, MOE_BF16>(uint4 w, const uint8_t* xrow, int c) {
-  const uint4 xv = ldg16(xrow + (size_t)c * 16);
-  float acc = dot2_bf16(w.x, xv.x, 0.f);
-  acc = dot2_bf16(w.y, xv.y, acc);
-  acc = dot2_bf16(w.z, xv.z, acc);
-  return dot2_bf16(w.w, xv.w, acc);
-}
-
-template <>
-__device__ __forceinline__ float chunk_dot<MOE_F32, MOE_F32>(uint4 w, const uint8_t* xrow, int c) {
-  const float4 xv = *(const float4*)(xrow + (size_t)c * 16);
-  float acc = __uint_as_float(w.x) * xv.x;
-  acc = fmaf(__uint_as_float(w.y), xv.y, acc);
-  acc = fmaf(__uint_as_float(w.z), xv.z, acc);
-  return fmaf(__uint_as_float(w.w), xv.w, acc);
-}
-
-__device__ __forceinline__ float fp4_dword_dot(uint32_t q, uint4 xv, float acc) {
-  acc = dot2_bf16(fp4x2_to_bf16x2<0>(q), xv.x, acc);
-  acc = dot2_bf16(fp4x2_to_bf16x2<1>(q), xv.y, acc);
-  acc = dot2_bf16(fp4x2_to_bf16x2<2>(q), xv.z, acc);
-  return dot2_bf16(fp4x2_to_bf16x2<3>(q), xv.w, acc);
-}
-
-template <>
-__device__ __forceinline__ float chunk_dot<MOE_MXFP4, MOE_BF16>(uint4 w, const uint8_t* xrow, int c) {
-  const uint8_t* xp = xrow + (size_t)c * 64;
-  float acc = fp4_dword_dot(w.x, ldg16(xp), 0.f);
-  acc = fp4_dword_dot(w.y, ldg16(xp + 16), acc);
-  acc = fp4_dword_dot(w.z, ldg16(xp + 32), acc);
-  return fp4_dword_dot(w.w, ldg16(xp + 48), acc);
-}
+// GUC<WT, XT>: the gate and up chunks of one row pair, unpacked once (deq), then dotted
+// with each routed token's x chunk; the x chunk is read once for both rows.
+template <int WT, int XT> struct GUC;
+template <> struct GUC<MOE_BF16, MOE_BF16> {
+  typedef uint4 D;
+  static __device__ __forceinline__ D deq(uint4 w) { return w; }
+  static __device__ __forceinline__ void dot(const D& g, const D& u, const uint8_t* xrow, int c,
+                                             float sg, float su, float& ag, float& au) {
+    const uint4 xv = ldg16(xrow + (size_t)c * 16);
+    float a = dot2_bf16(g.x, xv.x, 0.f), b = dot2_bf16(u.x, xv.x, 0.f);
+    a = dot2_bf16(g.y, xv.y, a);
+    b = dot2_bf16(u.y, xv.y, b);
+    a = dot2_bf16(g.z, xv.z, a);
+    b = dot2_bf16(u.z, xv.z, b);
+    a = dot2_bf16(g.w, xv.w, a);
+    b = dot2_bf16(u.w, xv.w, b);
+    ag = fmaf(sg, a, ag);
+    au = fmaf(su, b, au);
+  }
+};
+template <> struct GUC<MOE_F32, MOE_F32> {
+  typedef uint4 D;
+  static __device__ __forceinline__ D deq(uint4 w) { return w; }
+  static __device__ __forceinline__ void dot(const D& g, const D& u, const uint8_t* xrow, int c,
+                                             float sg, float su, float& ag, float& au) {
+    const float4 xv = *(const float4*)(xrow + (size_t)c * 16);
+    float a = __uint_as_float(g.x) * xv.x, b = __uint_as_float(u.x) * xv.x;
+    a = fmaf(__uint_as_float(g.y), xv.y, a);
+    b = fmaf(__uint_as_float(u.y), xv.y, b);
+    a = fmaf(__uint_as_float(g.z), xv.z, a);
+    b = fmaf(__uint_as_float(u.z), xv.z, b);
+    a = fmaf(__uint_as_float(g.w), xv.w, a);
+    b = fmaf(__uint_as_float(u.w), xv.w, b);
+    ag = fmaf(sg, a, ag);
+    au = fmaf(su, b, au);
+  }
+};
+// 32 e2m1 codes (one MX block) -> 16 bf16 pairs, exact at unit scale; the block scale is
+// applied to the chunk's dot product.
+template <> struct GUC<MOE_MXFP4, MOE_BF16> {
+  struct D { uint32_t v[16]; };
+  static __device__ __forceinline__ void deq4(uint32_t q, uint32_t* o) {
+    o[0] = fp4x2_to_bf16x2<0>(q);
+    o[1] = fp4x2_to_bf16x2<1>(q);
+    o[2] = fp4x2_to_bf16x2<2>(q);
+    o[3] = fp4x2_to_bf16x2<3>(q);
+  }
+  static __device__ __forceinline__ D deq(uint4 w) {
+    D d;
+    deq4(w.x, d.v);
+    deq4(w.y, d.v + 4);
+    deq4(w.z, d.v + 8);
+    deq4(w.w, d.v + 12);
+    return d;
+  }
+  static __device__ __forceinline__ void dot(const D& g, const D& u, const uint8_t* xrow, int c,
+                                             float sg, float su, float& ag, float& au) {
+    const uint8_t* xp = xrow + (size_t)c * 64;
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 xv = ldg16(xp + 16 * q);
+      a = dot2_bf16(g.v[4 * q + 0], xv.x, a);
+      b = dot2_bf16(u.v[4 * q + 0], xv.x, b);
+      a = dot2_bf16(g.v[4 * q + 1], xv.y, a);
+      b = dot2_bf16(u.v[4 * q + 1], xv.y, b);
+      a = dot2_bf16(g.v[4 * q + 2], xv.z, a);
+      b = dot2_bf16(u.v[4 * q + 2], xv.z, b);
+      a = dot2_bf16(g.v[4 * q + 3], xv.w, a);
+      b = dot2_bf16(u.v[4 * q + 3], xv.w, b);
+    }
+    ag = fmaf(sg, a, ag);
+    au = fmaf(su, b, au);
+  }
+};
 
 // One lane group (G lanes) computes gate and up row `row` (reduction over K = H) for every
 // token in `mask` and writes out[slot][row] = silu(g) * u.  All loads of a K-slice are issued
 // before any is consumed; lanes past the row end load a valid chunk and scale it by 0.
-template <int XT, int WT, int G, int NCH, int TM>
+// XL: the block first copies all T rows of x (xbytes) from xg into LDS at xs -- after its
+// first weight loads are in flight -- and reads x from there; every thread of the block
+// must call this function.
+template <int XT, int WT, int G, int NCH, int TM, bool XL>
 __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* urow,
                                            const uint8_t* gsrow, const uint8_t* usrow,
-                                           int nchunks, const uint8_t* xb, size_t xstride,
-                                           unsigned mask, const int* slots, float* out,
-                                           int out_ld, int row, int gl, bool valid) {
+                                           int nchunks, const uint8_t* xg, uint4* xs, int xbytes,
+                                           size_t xstride, unsigned mask, const int* slots,
+                                           float* out, int out_ld, int row, int gl, bool valid) {
+  typedef GUC<WT, XT> C;
   float ag[TM], au[TM];
 #pragma unroll
   for (int t = 0; t < TM; ++t) ag[t] = au[t] = 0.f;
   for (int c0 = 0; c0 < nchunks; c0 += G * NCH) {
     uint4 wg[NCH], wu[NCH];
-    float sg[NCH], su[NCH];
+    uint32_t bg[NCH], bu[NCH];  // e2m1: raw scale bytes, converted when the chunk is used
+    float okf[NCH];
     int cc[NCH];
 #pragma unroll
     for (int m = 0; m < NCH; ++m) {
       const int c = c0 + gl + G * m;
       const bool ok = valid && c < nchunks;
       cc[m] = ok ? c : 0;
+      okf[m] = ok ? 1.f : 0.f;
       wg[m] = ldg16(grow + (size_t)cc[m] * 16);
       wu[m] = ldg16(urow + (size_t)cc[m] * 16);
       if constexpr (WT == MOE_MXFP4) {
-        sg[m] = e8m0_to_f32(gsrow[cc[m]]);
-        su[m] = e8m0_to_f32(usrow[cc[m]]);
-      } else {
-        sg[m] = su[m] = 1.f;
+        bg[m] = gsrow[cc[m]];
+        bu[m] = usrow[cc[m]];
       }
-      if (!ok) sg[m] = su[m] = 0.f;
     }
+    if constexpr (XL) {
+      if (c0 == 0) {
+        for (int i = threadIdx.x; i < xbytes / 16; i += blockDim.x) xs[i] = ldg16(xg + (size_t)i * 16);
+        __syncthreads();
+      }
+    }
+    const uint8_t* xb = XL ? (const uint8_t*)xs : xg;
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      if (!((mask >> t) & 1u)) continue;  // uniform
-      const uint8_t* xrow = xb + (size_t)t * xstride;
+    for (int m = 0; m < NCH; ++m) {
+      const typename C::D dg = C::deq(wg[m]), du = C::deq(wu[m]);
+      float sg = okf[m], su = okf[m];
+      if constexpr (WT == MOE_MXFP4) {  // select, not multiply: a NaN scale must not leak
+        sg = okf[m] != 0.f ? e8m0_to_f32(bg[m]) : 0.f;
+        su = okf[m] != 0.f ? e8m0_to_f32(bu[m]) : 0.f;
+      }
 #pragma unroll
-      for (int m = 0; m < NCH; ++m) {
-        ag[t] = fmaf(sg[m], chunk_dot<WT, XT>(wg[m], xrow, cc[m]), ag[t]);
-        au[t] = fmaf(su[m], chunk_dot<WT, XT>(wu[m], xrow, cc[m]), au[t]);
+      for (int t = 0; t < TM; ++t) {
+        if (!((mask >> t) & 1u)) continue;  // uniform
+        C::dot(dg, du, xb + (size_t)t * xstride, cc[m], sg, su, ag[t], au[t]);
       }
     }
   }
@@ -129,47 +182,52 @@ __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* u
 }
 
 // ------------------------------------------------------------------------------------------
-// Down chunk arithmetic.  A chunk is 4 (fp32) or 8 (bf16, e2m1) consecutive elements of one
-// Wd row; the activation chunk is the same elements of a (fp32).
+// Down chunk arithmetic.  A chunk is 16 bytes of one Wd row: 4 fp32, 8 bf16 or 32 e2m1
+// elements; the activation chunk is the same elements of a (fp32).
 // ------------------------------------------------------------------------------------------
 template <int WT> struct DN;
 template <> struct DN<MOE_F32> {
   static constexpr int EPC = 4;
   typedef uint4 W;
   static __device__ __forceinline__ W load(const uint8_t* row, int c) { return ldg16(row + (size_t)c * 16); }
+  static __device__ __forceinline__ float dot_regs(W w, const float4* x) {
+    float acc = __uint_as_float(w.x) * x[0].x;
+    acc = fmaf(__uint_as_float(w.y), x[0].y, acc);
+    acc = fmaf(__uint_as_float(w.z), x[0].z, acc);
+    return fmaf(__uint_as_float(w.w), x[0].w, acc);
+  }
   static __device__ __forceinline__ float dot(W w, const float* a, int c) {
-    const float4 x = ldf4(a + (size_t)c * 4);
-    float acc = __uint_as_float(w.x) * x.x;
-    acc = fmaf(__uint_as_float(w.y), x.y, acc);
-    acc = fmaf(__uint_as_float(w.z), x.z, acc);
-    return fmaf(__uint_as_float(w.w), x.w, acc);
+    const float4 x[1] = {ldf4(a + (size_t)c * 4)};
+    return dot_regs(w, x);
   }
 };
 template <> struct DN<MOE_BF16> {
   static constexpr int EPC = 8;
   typedef uint4 W;
   static __device__ __forceinline__ W load(const uint8_t* row, int c) { return ldg16(row + (size_t)c * 16); }
+  static __device__ __forceinline__ float dot_regs(W w, const float4* x) {
+    float acc = bf16lo(w.x) * x[0].x;
+    acc = fmaf(bf16hi(w.x), x[0].y, acc);
+    acc = fmaf(bf16lo(w.y), x[0].z, acc);
+    acc = fmaf(bf16hi(w.y), x[0].w, acc);
+    acc = fmaf(bf16lo(w.z), x[1].x, acc);
+    acc = fmaf(bf16hi(w.z), x[1].y, acc);
+    acc = fmaf(bf16lo(w.w), x[1].z, acc);
+    return fmaf(bf16hi(w.w), x[1].w, acc);
+  }
   static __device__ __forceinline__ float dot(W w, const float* a, int c) {
-    const float4 x0 = ldf4(a + (size_t)c * 8), x1 = ldf4(a + (size_t)c * 8 + 4);
-    float acc = bf16lo(w.x) * x0.x;
-    acc = fmaf(bf16hi(w.x), x0.y, acc);
-    acc = fmaf(bf16lo(w.y), x0.z, acc);
-    acc = fmaf(bf16hi(w.y), x0.w, acc);
-    acc = fmaf(bf16lo(w.z), x1.x, acc);
-    acc = fmaf(bf16hi(w.z), x1.y, acc);
-    acc = fmaf(bf16lo(w.w), x1.z, acc);
-    return fmaf(bf16hi(w.w), x1.w, acc);
+    const float4 x[2] = {ldf4(a + (size_t)c * 8), ldf4(a + (size_t)c * 8 + 4)};
+    return dot_regs(w, x);
   }
 };
 template <> struct DN<MOE_MXFP4> {
-  static constexpr int EPC = 8;
-  typedef uint32_t W;
-  static __device__ __forceinline__ W load(const uint8_t* row, int c) { return ldg4(row + (size_t)c * 4); }
-  static __device__ __forceinline__ float dot(W w, const float* a, int c) {
-    const float4 x0 = ldf4(a + (size_t)c * 8), x1 = ldf4(a + (size_t)c * 8 + 4);
-    const f32x2_t p0 = fp4x2_to_f32x2<0>(w), p1 = fp4x2_to_f32x2<1>(w);
-    const f32x2_t p2 = fp4x2_to_f32x2<2>(w), p3 = fp4x2_to_f32x2<3>(w);
-    float acc = p0.x * x0.x;
+  static constexpr int EPC = 32;  // one MX block: 16 bytes of codes, one scale byte
+  typedef uint4 W;
+  static __device__ __forceinline__ W load(const uint8_t* row, int c) { return ldg16(row + (size_t)c * 16); }
+  static __device__ __forceinline__ float dword_dot(uint32_t q, float4 x0, float4 x1, float acc) {
+    const f32x2_t p0 = fp4x2_to_f32x2<0>(q), p1 = fp4x2_to_f32x2<1>(q);
+    const f32x2_t p2 = fp4x2_to_f32x2<2>(q), p3 = fp4x2_to_f32x2<3>(q);
+    acc = fmaf(p0.x, x0.x, acc);
     acc = fmaf(p0.y, x0.y, acc);
     acc = fmaf(p1.x, x0.z, acc);
     acc = fmaf(p1.y, x0.w, acc);
@@ -177,6 +235,19 @@ template <> struct DN<MOE_MXFP4> {
     acc = fmaf(p2.y, x1.y, acc);
     acc = fmaf(p3.x, x1.z, acc);
     return fmaf(p3.y, x1.w, acc);
+  }
+  static __device__ __forceinline__ float dot_regs(W w, const float4* x) {
+    float acc = dword_dot(w.x, x[0], x[1], 0.f);
+    acc = dword_dot(w.y, x[2], x[3], acc);
+    acc = dword_dot(w.z, x[4], x[5], acc);
+    return dword_dot(w.w, x[6], x[7], acc);
+  }
+  static __device__ __forceinline__ float dot(W w, const float* a, int c) {
+    const float* p = a + (size_t)c * 32;
+    float acc = dword_dot(w.x, ldf4(p), ldf4(p + 4), 0.f);
+    acc = dword_dot(w.y, ldf4(p + 8), ldf4(p + 12), acc);
+    acc = dword_dot(w.z, ldf4(p + 16), ldf4(p + 20), acc);
+    return dword_dot(w.w, ldf4(p + 24), ldf4(p + 28), acc);
   }
 };
 
@@ -194,7 +265,7 @@ constexpr int kWaves = kThreads / kWave;
 // Router logits (blocks [0, router_blocks)) and shared-expert gate/up (the rest).
 template <int XT, int SWT, int G, int NCH, int TM>
 __global__ __launch_bounds__(kThreads) void dec_stage1(Args A) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if ((int)blockIdx.x < A.router_blocks) {
     const int e = blockIdx.x * kWaves + wave;
     if (e >= A.E) return;
@@ -256,50 +327,161 @@ __global__ __launch_bounds__(kThreads) void dec_stage1(Args A) {
 #pragma unroll
     for (int t = 0; t < TM; ++t) slots[t] = t;
     const unsigned mask = (A.T >= 32) ? 0xffffffffu : ((1u << A.T) - 1u);
-    gateup_row<XT, SWT, G, NCH, TM>((const uint8_t*)A.sgate + r * rb, (const uint8_t*)A.sup + r * rb,
-                                    nullptr, nullptr, A.H / GU<SWT>::EPC, (const uint8_t*)A.x,
-                                    (size_t)A.H * XS<XT>::BYTES, mask, slots, A.a_sh, A.Is, row, gl,
-                                    valid);
+    gateup_row<XT, SWT, G, NCH, TM, false>((const uint8_t*)A.sgate + r * rb,
+                                           (const uint8_t*)A.sup + r * rb, nullptr, nullptr,
+                                           A.H / GU<SWT>::EPC, (const uint8_t*)A.x, nullptr, 0,
+                                           (size_t)A.H * XS<XT>::BYTES, mask, slots, A.a_sh, A.Is,
+                                           row, gl, valid);
   }
 }
 
-template <int XT, int WT, int G, int NCH, int TM>
-__global__ __launch_bounds__(kThreads) void dec_gateup(Args A, int tiles) {
+// Selection and the decode plan: one block, wave t selects token t (select_set: the k
+// largest logits, ties to the lower index, renormalised softmax weights), then the distinct
+// experts are compacted in ascending id with one ballot per 64 experts.
+__global__ __launch_bounds__(kWave * kDecodeMaxT) void dec_select(Args A) {
   __shared__ int s_ids[kDecodeMaxT * MOE_MAX_K];
   __shared__ float s_w[kDecodeMaxT * MOE_MAX_K];
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int s = blockIdx.x / tiles, tile = blockIdx.x - s * tiles;
-  const int T = A.T, k = A.k, S = T * k;
-  // selection of every token (one wave per token), identical in every block; each token's
-  // experts are listed in ascending index, which is also the slot order the down kernel reads
-  for (int t = wave; t < T; t += kWaves)
-    select_set(A.logits + (size_t)t * A.E, A.E, k, lane, s_ids + t * k, s_w + t * k);
+  __shared__ unsigned s_flag[MOE_MAX_E];
+  __shared__ int s_pos[MOE_MAX_E];
+  __shared__ int s_dslot[kDecodeMaxT * MOE_MAX_K * kDecodeMaxT];
+  __shared__ float s_dw[kDecodeMaxT * MOE_MAX_K * kDecodeMaxT];
+  __shared__ int s_nd;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave, nth = blockDim.x;
+  const int T = A.T, k = A.k, E = A.E, S = T * k, D = S < E ? S : E;
+  const DecodePlan P(A.plan, D, T);
+  for (int i = threadIdx.x; i < E; i += nth) s_flag[i] = 0u;
+  for (int i = threadIdx.x; i < D * T; i += nth) {
+    s_dslot[i] = 0;
+    s_dw[i] = 0.f;
+  }
+  if (wave < T) select_set(A.logits + (size_t)wave * E, E, k, lane, s_ids + wave * k, s_w + wave * k);
   __syncthreads();
-  if (blockIdx.x == 0) {  // publish the routing for the down kernel
-    for (int i = threadIdx.x; i < S; i += kThreads) {
-      A.ids[i] = s_ids[i];
-      A.cw[i] = s_w[i];
+  for (int i = threadIdx.x; i < S; i += nth) atomicOr(&s_flag[s_ids[i]], 1u << (i / k));
+  __syncthreads();
+  if (wave == 0) {
+    int cnt = 0;
+    for (int b = 0; b < E; b += kWave) {
+      const int e = b + lane;
+      const unsigned f = e < E ? s_flag[e] : 0u;
+      const uint64_t bal = __ballot(f != 0u);
+      const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+      if (f) {
+        s_pos[e] = pos;
+        P.dexp()[pos] = e;
+        P.dmask()[pos] = f;
+      }
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) {
+      s_nd = cnt;
+      *P.nd() = cnt;
     }
   }
-  // this block's expert and the tokens routed to it; only the first token's slot works
-  const int t0 = s / k, e = s_ids[s];
-  unsigned mask = 0;
-  int slots[TM];
-  bool owner = true;
+  __syncthreads();
+  // a token's k experts are distinct, so every (distinct expert, token) cell has one writer
+  for (int i = threadIdx.x; i < S; i += nth) {
+    const int c = s_pos[s_ids[i]] * T + i / k;
+    s_dslot[c] = i;
+    s_dw[c] = s_w[i];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < D * T; i += nth) {
+    P.dslot()[i] = s_dslot[i];
+    P.dw()[i] = s_dw[i];
+  }
+  for (int i = s_nd + threadIdx.x; i < D; i += nth) {
+    P.dexp()[i] = 0;
+    P.dmask()[i] = 0u;
+  }
+}
+
+// Shared expert's down projection, y_sh[t][h] = Wd_s[h] . a_s[t] (fp32), for 16 rows per
+// block (four per wave, 16 lanes per row).  It depends only on the stage-1 activations, so it
+// runs inside the gate/up kernel beside the routed rows, and the down kernel only adds it.
+constexpr int kShRowsPerBlock = kWaves * 4;
+template <int SWT, int TM>
+__device__ __forceinline__ void shared_down_rows(const Args& A, int blk, int lane, int wave) {
+  constexpr int G = 16, NCH = 2;
+  const int grp = lane / G, gl = lane % G;
+  const int h = blk * kShRowsPerBlock + wave * (kWave / G) + grp;
+  const bool valid = h < A.H;
+  const int nchs = A.Is / DN<SWT>::EPC;
+  const uint8_t* srow = (const uint8_t*)A.sdown + (size_t)(valid ? h : 0) * row_bytes<SWT>(A.Is);
+  float acc[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) acc[t] = 0.f;
+  for (int c0 = 0; c0 < nchs; c0 += G * NCH) {
+    typename DN<SWT>::W w[NCH];
+    int cc[NCH];
+    float okf[NCH];
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const int c = c0 + gl + G * m;
+      cc[m] = c < nchs ? c : 0;
+      okf[m] = c < nchs ? 1.f : 0.f;
+      w[m] = DN<SWT>::load(srow, cc[m]);
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t >= A.T) break;  // uniform
+#pragma unroll
+      for (int m = 0; m < NCH; ++m)
+        acc[t] = fmaf(okf[m], DN<SWT>::dot(w[m], A.a_sh + (size_t)t * A.Is, cc[m]), acc[t]);
+    }
+  }
 #pragma unroll
   for (int t = 0; t < TM; ++t) {
-    slots[t] = 0;
-    if (t < T) {
-      for (int j = 0; j < k; ++j) {
-        if (s_ids[t * k + j] == e) {
-          if (t < t0) owner = false;
-          mask |= 1u << t;
-          slots[t] = t * k + j;
-        }
-      }
-    }
+    const float v = group_sum<G>(acc[t]);
+    if (gl == 0 && valid && t < A.T) A.y_sh[(size_t)t * A.H + h] = v;
   }
-  if (!owner) return;
+}
+
+// Gate/up + SwiGLU: block (u, tile) streams RB rows per wave of distinct expert u's gate and
+// up matrices once and dots them with every token routed to u.  The first sh_blocks blocks
+// compute the shared expert's down projection instead.  XL: x is staged in LDS
+// (dynamic shared memory of T * H * sizeof(x) bytes).  SEL1 (T = 1, no selection kernel):
+// wave 0 of every block selects the token's experts from the logits itself -- the k experts
+// are then the distinct experts, in ascending id -- and block 0 publishes the plan for the
+// down kernel.
+template <int XT, int WT, int SWT, int G, int NCH, int TM, bool XL, bool SEL1>
+__global__ __launch_bounds__(kThreads) void dec_gateup(Args A, int tiles, int sh_blocks) {
+  extern __shared__ uint4 s_x[];
+  const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if ((int)blockIdx.x < sh_blocks) {
+    shared_down_rows<SWT, TM>(A, blockIdx.x, lane, wave);
+    return;
+  }
+  const int blk = blockIdx.x - sh_blocks;
+  const int u = blk / tiles, tile = blk - u * tiles;
+  const int T = A.T, S = T * A.k, D = S < A.E ? S : A.E;
+  const DecodePlan P(A.plan, D, T);
+  int e;
+  unsigned mask;
+  int slots[TM];
+  if constexpr (SEL1) {
+    __shared__ int s_ids[MOE_MAX_K];
+    __shared__ float s_w[MOE_MAX_K];
+    if (wave == 0) select_set(A.logits, A.E, A.k, lane, s_ids, s_w);
+    __syncthreads();
+    if (blk == 0 && threadIdx.x < A.k) {
+      const int i = threadIdx.x;
+      if (i == 0) *P.nd() = A.k;
+      P.dexp()[i] = s_ids[i];
+      P.dmask()[i] = 1u;
+      P.dslot()[i] = i;
+      P.dw()[i] = s_w[i];
+    }
+    e = s_ids[u];
+    mask = 1u;
+#pragma unroll
+    for (int t = 0; t < TM; ++t) slots[t] = u;
+  } else {
+    if (u >= *P.nd()) return;
+    e = P.dexp()[u];
+    mask = P.dmask()[u];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) slots[t] = t < T ? P.dslot()[u * T + t] : 0;
+  }
   constexpr int RB = kWave / G;
   const int grp = lane / G, gl = lane % G;
   const int row = tile * (kWaves * RB) + wave * RB + grp;
@@ -311,101 +493,160 @@ __global__ __launch_bounds__(kThreads) void dec_gateup(Args A, int tiles) {
     gsr = A.gs + r * (A.H / 32);
     usr = A.us + r * (A.H / 32);
   }
-  gateup_row<XT, WT, G, NCH, TM>((const uint8_t*)A.gate + r * rb, (const uint8_t*)A.up + r * rb, gsr,
-                                 usr, A.H / GU<WT>::EPC, (const uint8_t*)A.x,
-                                 (size_t)A.H * XS<XT>::BYTES, mask, slots, A.a, A.I, row, gl, valid);
+  const size_t xstride = (size_t)A.H * XS<XT>::BYTES;
+  gateup_row<XT, WT, G, NCH, TM, XL>((const uint8_t*)A.gate + r * rb, (const uint8_t*)A.up + r * rb,
+                                     gsr, usr, A.H / GU<WT>::EPC, (const uint8_t*)A.x, s_x,
+                                     (int)(T * xstride), xstride, mask, slots, A.a, A.I, row, gl,
+                                     valid);
 }
 
-template <int WT, int SWT, int G, int NCH, int TM, int US>
-__global__ __launch_bounds__(kThreads) void dec_down(Args A) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+// Down + combine: y[t][h] = sum over t's experts of w * (Wd[e][h] . a) + y_sh[t][h].
+// Output rows come in groups of RB (one lane group of G lanes per row); a block takes row
+// groups blockIdx.x, blockIdx.x + gridDim.x, ... and its NW waves share the work items
+// (row group, K-slice, distinct expert) round robin.  The plan and -- when it fits (ALDS) --
+// every routed activation row are staged in LDS once per block; each wave then streams its
+// items' 16-byte weight chunks with the next item's loads in flight while it consumes the
+// current one.  Per (row group, wave) partial sums go to LDS and are added in a fixed order
+// at the end, so the result is deterministic.
+// Dynamic LDS (4-byte words): plan (2D + 2DT), partials [nrgb_max][NW][TM][RB], then ALDS
+// activations [T*k][I].
+template <int WT, int G, int NCH, int TM, bool ALDS>
+__global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, int act_off) {
+  extern __shared__ float s_f[];
+  typedef typename DN<WT>::W W;
   constexpr int RB = kWave / G;
+  constexpr int EPC = DN<WT>::EPC;
+  const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int NW = blockDim.x / kWave;
   const int grp = lane / G, gl = lane % G;
-  const int h = blockIdx.x * RB + grp;
-  const bool valid = h < A.H;
-  const int hh = valid ? h : 0;
-  const int S = A.T * A.k;
-  const int nch = A.I / DN<WT>::EPC;
+  const int T = A.T, S = T * A.k, D = S < A.E ? S : A.E;
+  const DecodePlan P(A.plan, D, T);
+  int* s_e = (int*)s_f;
+  unsigned* s_m = (unsigned*)(s_f + D);
+  int* s_sl = (int*)(s_f + 2 * D);
+  float* s_w = s_f + 2 * D + D * T;
+  float* s_part = s_f + 2 * D + 2 * D * T;
+  float* s_act = s_f + act_off;
+  const int nd = *P.nd();
+  for (int i = threadIdx.x; i < D; i += blockDim.x) {
+    s_e[i] = P.dexp()[i];
+    s_m[i] = P.dmask()[i];
+  }
+  for (int i = threadIdx.x; i < D * T; i += blockDim.x) {
+    s_sl[i] = P.dslot()[i];
+    s_w[i] = P.dw()[i];
+  }
+  for (int i = threadIdx.x; i < nrgb_max * NW * TM * RB; i += blockDim.x) s_part[i] = 0.f;
+  if constexpr (ALDS) {
+    const int n4 = S * A.I / 4;
+    for (int i = threadIdx.x; i < n4; i += blockDim.x) ((float4*)s_act)[i] = ldf4(A.a + (size_t)i * 4);
+  }
+  __syncthreads();
+
+  const int nch = A.I / EPC;
+  const int nsl = (nch + G * NCH - 1) / (G * NCH);
+  const int per_rg = nsl * nd;
+  const int nrgb = (nrg - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
+  const int nq = nrgb * per_rg;
   const size_t rb = row_bytes<WT>(A.I);
+  const float* abase = ALDS ? s_act : A.a;
+
   float acc[TM];
 #pragma unroll
   for (int t = 0; t < TM; ++t) acc[t] = 0.f;
-
-  for (int c0 = 0; c0 < nch; c0 += G * NCH) {
-    int cc[NCH];
-    float okf[NCH];
+  int cur_j = -1;
+  // item q -> (row group j of this block, slice sl, distinct expert u)
+  auto item = [&](int q, int& j, int& sl, int& u) {
+    j = q / per_rg;
+    const int r = q - j * per_rg;
+    sl = r / nd;
+    u = r - sl * nd;
+  };
+  auto load = [&](int q, W* w, uint32_t* sb) {
+    int j, sl, u;
+    item(q, j, sl, u);
+    const int h = ((int)blockIdx.x + j * (int)gridDim.x) * RB + grp;
+    const int hh = h < A.H ? h : 0;
+    const int e = s_e[u];
+    const uint8_t* row = (const uint8_t*)A.down + ((size_t)e * A.H + hh) * rb;
 #pragma unroll
     for (int m = 0; m < NCH; ++m) {
-      const int c = c0 + gl + G * m;
+      const int c = sl * G * NCH + gl + G * m;
+      const int cc = c < nch ? c : 0;
+      w[m] = DN<WT>::load(row, cc);
+      if constexpr (WT == MOE_MXFP4) sb[m] = A.ds[((size_t)e * A.H + hh) * (A.I / 32) + cc];
+    }
+  };
+  auto flush = [&]() {
+    if (cur_j < 0) return;  // uniform
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const float v = group_sum<G>(acc[t]);
+      if (gl == 0) s_part[((cur_j * NW + wave) * TM + t) * RB + grp] = v;
+      acc[t] = 0.f;
+    }
+  };
+  auto consume = [&](int q, const W* w, const uint32_t* sb) {
+    int j, sl, u;
+    item(q, j, sl, u);
+    if (j != cur_j) {  // uniform
+      flush();
+      cur_j = j;
+    }
+    int cc[NCH];
+    float sc[NCH];
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const int c = sl * G * NCH + gl + G * m;
       cc[m] = c < nch ? c : 0;
-      okf[m] = c < nch ? 1.f : 0.f;
+      if constexpr (WT == MOE_MXFP4)  // select, not multiply: a NaN scale must not leak
+        sc[m] = c < nch ? e8m0_to_f32(sb[m]) : 0.f;
+      else
+        sc[m] = c < nch ? 1.f : 0.f;
     }
-    for (int s0 = wave; s0 < S; s0 += kWaves * US) {
-      typename DN<WT>::W wv[US][NCH];
-      float sc[US][NCH];
-      int eu[US];
+    const unsigned mask = s_m[u];
 #pragma unroll
-      for (int u = 0; u < US; ++u) eu[u] = A.ids[min(s0 + kWaves * u, S - 1)];
+    for (int t = 0; t < TM; ++t) {
+      if (!((mask >> t) & 1u)) continue;  // uniform
+      const float* arow = abase + (size_t)s_sl[u * T + t] * A.I;
+      float part = 0.f;
 #pragma unroll
-      for (int u = 0; u < US; ++u) {
-        const uint8_t* row = (const uint8_t*)A.down + ((size_t)eu[u] * A.H + hh) * rb;
+      for (int m = 0; m < NCH; ++m) part = fmaf(sc[m], DN<WT>::dot(w[m], arow, cc[m]), part);
+      acc[t] = fmaf(s_w[u * T + t], part, acc[t]);
+    }
+  };
+  int q = wave;
+  if (q < nq) {  // uniform
+    W cur[NCH];
+    uint32_t scur[NCH] = {};
+    load(q, cur, scur);
+    for (; q + NW < nq; q += NW) {
+      W nxt[NCH];
+      uint32_t snxt[NCH] = {};
+      load(q + NW, nxt, snxt);
+      consume(q, cur, scur);
 #pragma unroll
-        for (int m = 0; m < NCH; ++m) {
-          wv[u][m] = DN<WT>::load(row, cc[m]);
-          float scale = 1.f;
-          if constexpr (WT == MOE_MXFP4)
-            scale = e8m0_to_f32(A.ds[((size_t)eu[u] * A.H + hh) * (A.I / 32) + cc[m] / 4]);
-          sc[u][m] = okf[m] * scale;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < US; ++u) {
-        const int s = s0 + kWaves * u;
-        if (s < S) {  // uniform
-          const int t = s / A.k;
-          const float* arow = A.a + (size_t)s * A.I;
-          float part = 0.f;
-#pragma unroll
-          for (int m = 0; m < NCH; ++m) part = fmaf(sc[u][m], DN<WT>::dot(wv[u][m], arow, cc[m]), part);
-          part *= A.cw[s];
-#pragma unroll
-          for (int tt = 0; tt < TM; ++tt) acc[tt] += (tt == t) ? part : 0.f;
-        }
+      for (int m = 0; m < NCH; ++m) {
+        cur[m] = nxt[m];
+        scur[m] = snxt[m];
       }
     }
-  }
-  // shared expert: its chunks are split over the block's waves
-  if (A.Is > 0) {
-    const int nchs = A.Is / DN<SWT>::EPC;
-    const uint8_t* srow = (const uint8_t*)A.sdown + (size_t)hh * row_bytes<SWT>(A.Is);
-    for (int cb = wave * G; cb < nchs; cb += kWaves * G) {
-      const int c = cb + gl;
-      const int ccs = c < nchs ? c : 0;
-      const float okf = c < nchs ? 1.f : 0.f;
-      const typename DN<SWT>::W w = DN<SWT>::load(srow, ccs);
-#pragma unroll
-      for (int t = 0; t < TM; ++t)
-        if (t < A.T) acc[t] = fmaf(okf, DN<SWT>::dot(w, A.a_sh + (size_t)t * A.Is, ccs), acc[t]);
-    }
-  }
-  __shared__ float s_part[kWaves][TM][RB];
-#pragma unroll
-  for (int t = 0; t < TM; ++t) {
-    const float v = group_sum<G>(acc[t]);
-    if (gl == 0) s_part[wave][t][grp] = v;
+    consume(q, cur, scur);
+    flush();
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < TM * RB; i += kThreads) {
-    const int t = i / RB, g = i % RB;
-    const int ho = blockIdx.x * RB + g;
-    if (t < A.T && ho < A.H) {
-      float v = s_part[0][t][g];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) v += s_part[w][t][g];
+  for (int i = threadIdx.x; i < nrgb * TM * RB; i += blockDim.x) {
+    const int j = i / (TM * RB), r = i - j * (TM * RB);
+    const int t = r / RB, g = r - t * RB;
+    const int h = ((int)blockIdx.x + j * (int)gridDim.x) * RB + g;
+    if (t < T && h < A.H) {
+      float v = 0.f;
+      for (int w = 0; w < NW; ++w) v += s_part[((j * NW + w) * TM + t) * RB + g];
+      if (A.Is > 0) v += A.y_sh[(size_t)t * A.H + h];
       if (A.odt == MOE_BF16)
-        ((uint16_t*)A.y)[(size_t)t * A.H + ho] = f32_to_bf16(v);
+        ((uint16_t*)A.y)[(size_t)t * A.H + h] = f32_to_bf16(v);
       else
-        ((float*)A.y)[(size_t)t * A.H + ho] = v;
+        ((float*)A.y)[(size_t)t * A.H + h] = v;
     }
   }
 }
@@ -418,15 +659,39 @@ struct GN { int G, NCH; };
 // wider groups when several tokens share the x registers
 constexpr GN kGU1[] = {{32, 8}, {64, 4}, {64, 5}, {16, 5}, {16, 4}, {32, 1}, {16, 1}, {64, 1}, {64, 2}, {64, 8}};
 constexpr GN kGUn[] = {{64, 4}, {64, 5}, {16, 5}, {16, 4}, {64, 1}, {64, 2}, {32, 1}, {16, 1}, {32, 8}, {64, 8}};
-// down (reduction over I): four rows per wave
-constexpr GN kDN[] = {{16, 4}, {16, 6}, {16, 5}, {16, 3}, {16, 8}, {16, 2}, {16, 1}, {64, 8}};
+// down (reduction over I): activations come from LDS, so several chunks per lane are cheap;
+// the launcher prefers the entry that spreads the output rows most evenly over the CUs
+constexpr GN kDN[] = {{8, 3}, {8, 2}, {16, 4}, {32, 3}, {16, 3}, {8, 4}, {16, 2}, {32, 2},
+                      {16, 1}, {32, 1}, {8, 1}, {64, 8}};
 constexpr int kNGU = sizeof(kGU1) / sizeof(kGU1[0]);
 constexpr int kNDN = sizeof(kDN) / sizeof(kDN[0]);
 
+struct DevInfo { int ncu, max_lds; };
+DevInfo dev_info() {
+  static DevInfo cache[64];
+  static bool have[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!have[dev]) {
+    int ncu = 0, lds = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lds <= 0) lds = 65536;
+    cache[dev] = DevInfo{ncu, lds};
+    have[dev] = true;
+  }
+  return cache[dev];
+}
+
 // First entry with the fewest idle chunk slots; the last entry (64, 8) walks long rows in
 // slices when nothing covers the row.
+// first_fit: the first entry that leaves at most a quarter of its chunk slots idle.
 template <int N>
-int pick_gn(const GN (&list)[N], int nchunks) {
+int pick_gn(const GN (&list)[N], int nchunks, bool first_fit = false) {
+  if (first_fit)
+    for (int i = 0; i < N; ++i) {
+      const int cap = list[i].G * list[i].NCH;
+      if (cap >= nchunks && 4 * (cap - nchunks) <= cap) return i;
+    }
   int best = N - 1, waste = 1 << 30;
   for (int i = 0; i < N; ++i) {
     const int cap = list[i].G * list[i].NCH;
@@ -439,6 +704,23 @@ int pick_gn(const GN (&list)[N], int nchunks) {
   return best;
 }
 
+// Down config: among entries leaving at most a quarter of their chunk slots idle, the one
+// with the fewest output rows on the busiest CU (ties: list order); else the fewest idle.
+int pick_down(int nchunks, int H, int ncu) {
+  int best = -1, score = 1 << 30;
+  for (int i = 0; i < kNDN; ++i) {
+    const int cap = kDN[i].G * kDN[i].NCH;
+    if (cap < nchunks || 4 * (cap - nchunks) > cap) continue;
+    const int rb = kWave / kDN[i].G, nrg = (H + rb - 1) / rb;
+    const int sc = ((nrg + ncu - 1) / ncu) * rb;
+    if (sc < score) {
+      best = i;
+      score = sc;
+    }
+  }
+  return best >= 0 ? best : pick_gn(kDN, nchunks);
+}
+
 template <int XT, int SWT, int TM, const GN* L>
 void* stage1_fn(int gi) {
   switch (gi) {
@@ -448,44 +730,39 @@ void* stage1_fn(int gi) {
   }
   return nullptr;
 }
-template <int XT, int WT, int TM, const GN* L>
+template <int XT, int WT, int SWT, int TM, const GN* L, bool XL, bool SEL1>
 void* gateup_fn(int gi) {
   switch (gi) {
-#define C(i) case i: return (void*)dec_gateup<XT, WT, L[i].G, L[i].NCH, TM>;
+#define C(i) case i: return (void*)dec_gateup<XT, WT, SWT, L[i].G, L[i].NCH, TM, XL, SEL1>;
     C(0) C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8) C(9)
 #undef C
   }
   return nullptr;
 }
-template <int WT, int SWT, int TM>
+template <int WT, int TM, bool ALDS>
 void* down_fn(int gi) {
   switch (gi) {
-#define C(i) case i: return (void*)dec_down<WT, SWT, kDN[i].G, kDN[i].NCH, TM, (kDN[i].NCH >= 6 ? 1 : 2)>;
-    C(0) C(1) C(2) C(3) C(4) C(5) C(6) C(7)
+#define C(i) case i: return (void*)dec_down<WT, kDN[i].G, kDN[i].NCH, TM, ALDS>;
+    C(0) C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8) C(9) C(10) C(11)
 #undef C
   }
   return nullptr;
 }
 
 int gu_epc(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : 32; }
-int dn_epc(int dt) { return dt == MOE_F32 ? 4 : 8; }
+int dn_epc(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : 32; }
+constexpr int kMaxLdsX = 64 * 1024;  // x staged in LDS by the gate/up kernel up to this size
 
 template <int XT, int WT, int SWT, int TM>
 int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& hook) {
   constexpr const GN* GUL = TM == 1 ? kGU1 : kGUn;
-  const int S = A.T * A.k;
+  const DevInfo dv = dev_info();
+  const int S = A.T * A.k, D = S < A.E ? S : A.E;
   const int g1 = pick_gn(TM == 1 ? kGU1 : kGUn, A.H / gu_epc(SWT));
   const int rb1 = kWaves * (kWave / GUL[g1].G);
   A.router_blocks = (A.E + kWaves - 1) / kWaves;
   A.shared_blocks = (route_only || A.Is == 0) ? 0 : (A.Is + rb1 - 1) / rb1;
-  const int g2 = pick_gn(TM == 1 ? kGU1 : kGUn, A.H / gu_epc(WT));
-  const int rb2 = kWaves * (kWave / GUL[g2].G);
-  const int tiles = (A.I + rb2 - 1) / rb2;
-  const int g3 = pick_gn(kDN, A.I / dn_epc(WT));
-  const int rb3 = kWave / kDN[g3].G;
   void* f1 = stage1_fn<XT, SWT, TM, GUL>(g1);
-  void* f2 = gateup_fn<XT, WT, TM, GUL>(g2);
-  void* f3 = down_fn<WT, SWT, TM>(g3);
 
   void* args1[] = {&A};
   hook.pre("dec_router_shared", st);
@@ -494,16 +771,48 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   if (err != hipSuccess) return MOE_EHIP;
   if (route_only) return MOE_OK;
 
-  int tl = tiles;
-  void* args2[] = {&A, &tl};
+  if (TM > 1) {  // T = 1 selects inside the gate/up kernel
+    hook.pre("dec_select", st);
+    err = hipLaunchKernel((void*)dec_select, dim3(1), dim3(kWave * A.T), args1, 0, st);
+    hook.post(st);
+    if (err != hipSuccess) return MOE_EHIP;
+  }
+
+  // gate/up: shared-expert down blocks first, then (distinct expert, row tile) blocks
+  const int g2 = pick_gn(TM == 1 ? kGU1 : kGUn, A.H / gu_epc(WT));
+  const int rb2 = kWaves * (kWave / GUL[g2].G);
+  int tiles = (A.I + rb2 - 1) / rb2;
+  int sh_blocks = A.Is > 0 ? (A.H + kShRowsPerBlock - 1) / kShRowsPerBlock : 0;
+  // x goes through LDS where one weight chunk meets many x bytes (e2m1: 64 per 16)
+  const size_t xbytes = (size_t)A.T * A.H * (XT == MOE_F32 ? 4 : 2);
+  const bool xl = TM > 1 && WT == MOE_MXFP4 && xbytes <= kMaxLdsX;
+  void* f2 = TM == 1 ? gateup_fn<XT, WT, SWT, TM, GUL, false, true>(g2)
+             : xl    ? gateup_fn<XT, WT, SWT, TM, GUL, true, false>(g2)
+                     : gateup_fn<XT, WT, SWT, TM, GUL, false, false>(g2);
+  void* args2[] = {&A, &tiles, &sh_blocks};
   hook.pre("dec_gateup", st);
-  err = hipLaunchKernel(f2, dim3(S * tiles), dim3(kThreads), args2, 0, st);
+  err = hipLaunchKernel(f2, dim3(sh_blocks + D * tiles), dim3(kThreads), args2, xl ? xbytes : 0, st);
   hook.post(st);
   if (err != hipSuccess) return MOE_EHIP;
 
-  void* args3[] = {&A};
+  // down: at most one block per CU, each over an even share of the row groups
+  const int g3 = pick_down(A.I / dn_epc(WT), A.H, dv.ncu);
+  const int rb3 = kWave / kDN[g3].G;
+  int nrg = (A.H + rb3 - 1) / rb3;
+  int nrgb = (nrg + dv.ncu - 1) / dv.ncu;
+  const int grid3 = (nrg + nrgb - 1) / nrgb;
+  constexpr int nw = 16;
+  const size_t plan_w = 2 * (size_t)D + 2 * (size_t)D * A.T;
+  int act_off = (int)((plan_w + (size_t)nrgb * nw * TM * rb3 + 3) / 4 * 4);
+  const size_t lds_act = (size_t)act_off * 4 + (size_t)S * A.I * 4;
+  const bool alds = lds_act <= (size_t)dv.max_lds;
+  const size_t lds3 = alds ? lds_act : (size_t)act_off * 4;
+  void* f3 = alds ? down_fn<WT, TM, true>(g3) : down_fn<WT, TM, false>(g3);
+  if (lds3 > 65536 && hipFuncSetAttribute(f3, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3) != hipSuccess)
+    return MOE_EHIP;
+  void* args3[] = {&A, &nrg, &nrgb, &act_off};
   hook.pre("dec_down", st);
-  err = hipLaunchKernel(f3, dim3((A.H + rb3 - 1) / rb3), dim3(kThreads), args3, 0, st);
+  err = hipLaunchKernel(f3, dim3(grid3), dim3(kWave * nw), args3, lds3, st);
   hook.post(st);
   if (err != hipSuccess) return MOE_EHIP;
   return MOE_OK;
