@@ -18,6 +18,9 @@
 //           experts and reduce through LDS in a fixed order, so results are deterministic.
 #pragma once
 
+#include <algorithm>
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 #include "select.h"
@@ -119,9 +122,9 @@ template <> struct GUC<MOE_MXFP4, MOE_BF16> {
 // One lane group (G lanes) computes gate and up row `row` (reduction over K = H) for every
 // token in `mask` and writes out[slot][row] = silu(g) * u.  All loads of a K-slice are issued
 // before any is consumed; lanes past the row end load a valid chunk and scale it by 0.
-// XL: the block first copies all T rows of x (xbytes) from xg into LDS at xs -- after its
-// first weight loads are in flight -- and reads x from there; every thread of the block
-// must call this function.
+// XL: the block first copies the rows of x of the tokens in `mask` from xg into LDS at xs
+// (row t at t * xstride) -- after its first weight loads are in flight -- and reads x from
+// there; every thread of the block must call this function with the same mask.
 template <int XT, int WT, int G, int NCH, int TM, bool XL>
 __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* urow,
                                            const uint8_t* gsrow, const uint8_t* usrow,
@@ -151,8 +154,13 @@ __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* u
       }
     }
     if constexpr (XL) {
-      if (c0 == 0) {
-        for (int i = threadIdx.x; i < xbytes / 16; i += blockDim.x) xs[i] = ldg16(xg + (size_t)i * 16);
+      if (c0 == 0) {  // the rows of the tokens in `mask` only
+        const int rw = (int)(xstride / 16);
+        for (int t = 0; t < TM; ++t) {
+          if (!((mask >> t) & 1u)) continue;  // uniform
+          for (int i = threadIdx.x; i < rw; i += blockDim.x)
+            xs[t * rw + i] = ldg16(xg + (size_t)t * xstride + (size_t)i * 16);
+        }
         __syncthreads();
       }
     }
@@ -263,8 +271,9 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
 // Router logits (blocks [0, router_blocks)) and shared-expert gate/up (the rest).
-template <int XT, int SWT, int G, int NCH, int TM>
+template <int XT, int SWT, int G, int NCH, int TM, bool XL>
 __global__ __launch_bounds__(kThreads) void dec_stage1(Args A) {
+  extern __shared__ uint4 s_x1[];
   const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if ((int)blockIdx.x < A.router_blocks) {
     const int e = blockIdx.x * kWaves + wave;
@@ -289,20 +298,21 @@ __global__ __launch_bounds__(kThreads) void dec_stage1(Args A) {
       const float4 w = ldf4(wr + (size_t)c * 4);
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
-        if (t < A.T) {
-          float x0, x1, x2, x3;
-          if constexpr (XT == MOE_F32) {
-            const float4 xv = *(const float4*)(xb + t * xstride + (size_t)c * 16);
-            x0 = xv.x; x1 = xv.y; x2 = xv.z; x3 = xv.w;
-          } else {
-            const uint2 xv = ldg8(xb + t * xstride + (size_t)c * 8);
-            x0 = bf16lo(xv.x); x1 = bf16hi(xv.x); x2 = bf16lo(xv.y); x3 = bf16hi(xv.y);
-          }
-          acc[t] = fmaf(w.x, x0, acc[t]);
-          acc[t] = fmaf(w.y, x1, acc[t]);
-          acc[t] = fmaf(w.z, x2, acc[t]);
-          acc[t] = fmaf(w.w, x3, acc[t]);
+        // no branch around the x loads, so that they issue together with the weight loads;
+        // rows past T read row 0 and are never stored
+        const int tt = t < A.T ? t : 0;
+        float x0, x1, x2, x3;
+        if constexpr (XT == MOE_F32) {
+          const float4 xv = *(const float4*)(xb + tt * xstride + (size_t)c * 16);
+          x0 = xv.x; x1 = xv.y; x2 = xv.z; x3 = xv.w;
+        } else {
+          const uint2 xv = ldg8(xb + tt * xstride + (size_t)c * 8);
+          x0 = bf16lo(xv.x); x1 = bf16hi(xv.x); x2 = bf16lo(xv.y); x3 = bf16hi(xv.y);
         }
+        acc[t] = fmaf(w.x, x0, acc[t]);
+        acc[t] = fmaf(w.y, x1, acc[t]);
+        acc[t] = fmaf(w.z, x2, acc[t]);
+        acc[t] = fmaf(w.w, x3, acc[t]);
       }
     }
 #pragma unroll
@@ -327,11 +337,12 @@ __global__ __launch_bounds__(kThreads) void dec_stage1(Args A) {
 #pragma unroll
     for (int t = 0; t < TM; ++t) slots[t] = t;
     const unsigned mask = (A.T >= 32) ? 0xffffffffu : ((1u << A.T) - 1u);
-    gateup_row<XT, SWT, G, NCH, TM, false>((const uint8_t*)A.sgate + r * rb,
-                                           (const uint8_t*)A.sup + r * rb, nullptr, nullptr,
-                                           A.H / GU<SWT>::EPC, (const uint8_t*)A.x, nullptr, 0,
-                                           (size_t)A.H * XS<XT>::BYTES, mask, slots, A.a_sh, A.Is,
-                                           row, gl, valid);
+    const size_t xstride = (size_t)A.H * XS<XT>::BYTES;
+    gateup_row<XT, SWT, G, NCH, TM, XL>((const uint8_t*)A.sgate + r * rb,
+                                        (const uint8_t*)A.sup + r * rb, nullptr, nullptr,
+                                        A.H / GU<SWT>::EPC, (const uint8_t*)A.x, s_x1,
+                                        (int)(A.T * xstride), xstride, mask, slots, A.a_sh, A.Is,
+                                        row, gl, valid);
   }
 }
 
@@ -354,7 +365,9 @@ __global__ __launch_bounds__(kWave * kDecodeMaxT) void dec_select(Args A) {
     s_dslot[i] = 0;
     s_dw[i] = 0.f;
   }
-  if (wave < T) select_set(A.logits + (size_t)wave * E, E, k, lane, s_ids + wave * k, s_w + wave * k);
+  __shared__ unsigned s_hist[kDecodeMaxT][512];
+  if (wave < T)
+    select_set(A.logits + (size_t)wave * E, E, k, lane, s_hist[wave], s_ids + wave * k, s_w + wave * k);
   __syncthreads();
   for (int i = threadIdx.x; i < S; i += nth) atomicOr(&s_flag[s_ids[i]], 1u << (i / k));
   __syncthreads();
@@ -392,6 +405,27 @@ __global__ __launch_bounds__(kWave * kDecodeMaxT) void dec_select(Args A) {
   for (int i = s_nd + threadIdx.x; i < D; i += nth) {
     P.dexp()[i] = 0;
     P.dmask()[i] = 0u;
+  }
+}
+
+// Streams np steps of a wave with two register buffers used in turn: step p + 1 is loaded
+// before step p is consumed, and no buffer is ever copied into the other (a register copy
+// would wait for the copied loads).  At the end the last step is loaded once more (cache-
+// resident) instead of branching around the load, which keeps the wait counts exact.
+template <class Buf, class Load, class Consume>
+__device__ __forceinline__ void stream_steps(int np, Load load, Consume consume) {
+  if (np <= 0) return;  // uniform
+  Buf a, b;
+  load(0, a);
+  for (int p = 0;; p += 2) {
+    const bool more1 = p + 1 < np;
+    load(more1 ? p + 1 : p, b);
+    consume(p, a);
+    if (!more1) break;
+    const bool more2 = p + 2 < np;
+    load(more2 ? p + 2 : p + 1, a);
+    consume(p + 1, b);
+    if (!more2) break;
   }
 }
 
@@ -461,7 +495,8 @@ __global__ __launch_bounds__(kThreads) void dec_gateup(Args A, int tiles, int sh
   if constexpr (SEL1) {
     __shared__ int s_ids[MOE_MAX_K];
     __shared__ float s_w[MOE_MAX_K];
-    if (wave == 0) select_set(A.logits, A.E, A.k, lane, s_ids, s_w);
+    __shared__ unsigned s_hist[512];
+    if (wave == 0) select_set(A.logits, A.E, A.k, lane, s_hist, s_ids, s_w);
     __syncthreads();
     if (blk == 0 && threadIdx.x < A.k) {
       const int i = threadIdx.x;
@@ -562,7 +597,13 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
     sl = r / nd;
     u = r - sl * nd;
   };
-  auto load = [&](int q, W* w, uint32_t* sb) {
+  struct Buf {
+    W w[NCH];
+    uint32_t sb[NCH];
+  };
+  auto load = [&](int q, Buf& bf) {
+    W* w = bf.w;
+    uint32_t* sb = bf.sb;
     int j, sl, u;
     item(q, j, sl, u);
     const int h = ((int)blockIdx.x + j * (int)gridDim.x) * RB + grp;
@@ -586,7 +627,9 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
       acc[t] = 0.f;
     }
   };
-  auto consume = [&](int q, const W* w, const uint32_t* sb) {
+  auto consume = [&](int q, const Buf& bf) {
+    const W* w = bf.w;
+    const uint32_t* sb = bf.sb;
     int j, sl, u;
     item(q, j, sl, u);
     if (j != cur_j) {  // uniform
@@ -615,25 +658,11 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
       acc[t] = fmaf(s_w[u * T + t], part, acc[t]);
     }
   };
-  int q = wave;
-  if (q < nq) {  // uniform
-    W cur[NCH];
-    uint32_t scur[NCH] = {};
-    load(q, cur, scur);
-    for (; q + NW < nq; q += NW) {
-      W nxt[NCH];
-      uint32_t snxt[NCH] = {};
-      load(q + NW, nxt, snxt);
-      consume(q, cur, scur);
-#pragma unroll
-      for (int m = 0; m < NCH; ++m) {
-        cur[m] = nxt[m];
-        scur[m] = snxt[m];
-      }
-    }
-    consume(q, cur, scur);
-    flush();
-  }
+  // this wave's items are q = wave + NW * step
+  const int nmine = wave < nq ? (nq - 1 - wave) / NW + 1 : 0;
+  stream_steps<Buf>(nmine, [&](int st, Buf& bf) { load(wave + NW * st, bf); },
+                    [&](int st, const Buf& bf) { consume(wave + NW * st, bf); });
+  if (nmine > 0) flush();
   __syncthreads();
   for (int i = threadIdx.x; i < nrgb * TM * RB; i += blockDim.x) {
     const int j = i / (TM * RB), r = i - j * (TM * RB);
@@ -721,10 +750,25 @@ int pick_down(int nchunks, int H, int ncu) {
   return best >= 0 ? best : pick_gn(kDN, nchunks);
 }
 
-template <int XT, int SWT, int TM, const GN* L>
+// Resident blocks per CU of kernel f at this block size and dynamic LDS (cached).
+int blocks_per_cu(const void* f, int threads, size_t lds) {
+  struct E { const void* f; int threads; size_t lds; int n; };
+  static E cache[256];
+  static int used = 0;
+  static std::mutex mu;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].f == f && cache[i].threads == threads && cache[i].lds == lds) return cache[i].n;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, threads, lds) != hipSuccess || n < 1) n = 1;
+  if (used < 256) cache[used++] = E{f, threads, lds, n};
+  return n;
+}
+
+template <int XT, int SWT, int TM, const GN* L, bool XL>
 void* stage1_fn(int gi) {
   switch (gi) {
-#define C(i) case i: return (void*)dec_stage1<XT, SWT, L[i].G, L[i].NCH, TM>;
+#define C(i) case i: return (void*)dec_stage1<XT, SWT, L[i].G, L[i].NCH, TM, XL>;
     C(0) C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8) C(9)
 #undef C
   }
@@ -762,11 +806,15 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   const int rb1 = kWaves * (kWave / GUL[g1].G);
   A.router_blocks = (A.E + kWaves - 1) / kWaves;
   A.shared_blocks = (route_only || A.Is == 0) ? 0 : (A.Is + rb1 - 1) / rb1;
-  void* f1 = stage1_fn<XT, SWT, TM, GUL>(g1);
+  // x goes through LDS where several tokens meet each weight chunk
+  const size_t xbytes = (size_t)A.T * A.H * (XT == MOE_F32 ? 4 : 2);
+  const bool xl = TM > 1 && xbytes <= kMaxLdsX;
+  void* f1 = xl ? stage1_fn<XT, SWT, TM, GUL, true>(g1) : stage1_fn<XT, SWT, TM, GUL, false>(g1);
 
   void* args1[] = {&A};
   hook.pre("dec_router_shared", st);
-  hipError_t err = hipLaunchKernel(f1, dim3(A.router_blocks + A.shared_blocks), dim3(kThreads), args1, 0, st);
+  hipError_t err = hipLaunchKernel(f1, dim3(A.router_blocks + A.shared_blocks), dim3(kThreads), args1,
+                                   xl ? xbytes : 0, st);
   hook.post(st);
   if (err != hipSuccess) return MOE_EHIP;
   if (route_only) return MOE_OK;
@@ -783,9 +831,6 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   const int rb2 = kWaves * (kWave / GUL[g2].G);
   int tiles = (A.I + rb2 - 1) / rb2;
   int sh_blocks = A.Is > 0 ? (A.H + kShRowsPerBlock - 1) / kShRowsPerBlock : 0;
-  // x goes through LDS where one weight chunk meets many x bytes (e2m1: 64 per 16)
-  const size_t xbytes = (size_t)A.T * A.H * (XT == MOE_F32 ? 4 : 2);
-  const bool xl = TM > 1 && WT == MOE_MXFP4 && xbytes <= kMaxLdsX;
   void* f2 = TM == 1 ? gateup_fn<XT, WT, SWT, TM, GUL, false, true>(g2)
              : xl    ? gateup_fn<XT, WT, SWT, TM, GUL, true, false>(g2)
                      : gateup_fn<XT, WT, SWT, TM, GUL, false, false>(g2);

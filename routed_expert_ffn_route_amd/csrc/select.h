@@ -114,70 +114,109 @@ __device__ __forceinline__ void select_token(const float* lrow, int E, int k, in
     select_token_nv<16>(lrow, E, k, lane, ids_out, w_out);
 }
 
+// Inclusive prefix sum over the 64 lanes: a 16-lane Hillis-Steele scan on DPP row shifts,
+// then each row adds the last lane of the rows below it (row_bcast 15 and 31).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
+  return v;
+}
+
 // The same selection as a SET, listed in ascending expert index (not by rank), for kernels
-// that only need which experts a token uses and their weights.  The k-th largest key is
-// found by a binary search over its bits with wave ballots (stopping as soon as exactly k
-// keys pass), ties at the threshold go to the lowest indices, and every lane places its
-// chosen experts by a prefix count of the chosen bits.  Lanes write ids_out[pos] and
-// w_out[pos] for pos < k.
+// that only need which experts a token uses and their weights.  The k-th largest 32-bit
+// order key is found by a radix select, eight bits per pass from the top: each pass counts
+// the candidates' next digit in a 256-bin LDS histogram (hist: 512 words private to the
+// wave), a prefix sum over the bins taken from the largest digit down locates the digit that
+// holds the k-th key, and the candidates narrow to that digit; the search stops as soon as
+// that digit's whole bin is taken.  Ties at the threshold go to the lowest indices; every
+// lane places its chosen experts by a prefix count of the chosen bits.  Lanes write
+// ids_out[pos] and w_out[pos] for pos < k.
 template <int NV>
-__device__ __forceinline__ void select_set_nv(const float* lrow, int E, int k, int lane, int* ids_out,
-                                              float* w_out) {
+__device__ __forceinline__ void select_set_nv(const float* lrow, int E, int k, int lane, unsigned* hist,
+                                              int* ids_out, float* w_out) {
   uint32_t key[NV];
   float val[NV];
+  bool ok[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + kWave * i;
-    const bool ok = e < E;
-    val[i] = lrow[ok ? e : 0];
-    key[i] = ok ? f32_order_key(val[i]) : 0u;
+    ok[i] = e < E;
+    val[i] = lrow[ok[i] ? e : 0];
+    key[i] = f32_order_key(val[i]);
   }
-  // largest tau with count(key >= tau) >= k
-  uint32_t tau = 0;
-  int cnt_tau = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = tau | (1u << b);
-    int cnt = 0;
+  // hist[b] counts digit 255 - b, so lane l's four words hold digits 255-4l down to 252-4l.
+  // Two histograms alternate; each is cleared right after it is read, off the critical path.
+  ((uint4*)hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+  ((uint4*)hist)[kWave + lane] = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t prefix = 0;
+  int need = k;  // rank of the wanted key among the remaining candidates
+  int shift = 24;
+  for (int p = 0; p < 4; ++p, shift -= 8) {
+    unsigned* hp = hist + 256 * (p & 1);
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int i = 0; i < NV; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-    if (cnt >= k) {
-      tau = cand;
-      cnt_tau = cnt;
-      if (cnt == k) break;  // exactly k keys at or above: no tie to resolve
+    for (int i = 0; i < NV; ++i) {
+      const bool cand = ok[i] && (p == 0 || (key[i] >> (shift + 8)) == prefix);
+      if (cand) atomicAdd(&hp[255u - ((key[i] >> shift) & 255u)], 1u);
     }
+    __builtin_amdgcn_wave_barrier();
+    const uint4 h = ((const uint4*)hp)[lane];
+    ((uint4*)hp)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    const int sum = (int)(h.x + h.y + h.z + h.w);
+    const int incl = wave_incl_scan(sum);
+    const uint64_t hit = __ballot(incl >= need);
+    const int L = __builtin_ctzll(hit);  // the wanted key's digit is in lane L's bins
+    int above = __builtin_amdgcn_readlane(incl - sum, L);
+    const int c0 = __builtin_amdgcn_readlane((int)h.x, L), c1 = __builtin_amdgcn_readlane((int)h.y, L);
+    const int c2 = __builtin_amdgcn_readlane((int)h.z, L), c3 = __builtin_amdgcn_readlane((int)h.w, L);
+    int j = 0, c = c0;
+    if (above + c0 < need) {
+      above += c0;
+      j = 1;
+      c = c1;
+      if (above + c1 < need) {
+        above += c1;
+        j = 2;
+        c = c2;
+        if (above + c2 < need) {
+          above += c2;
+          j = 3;
+          c = c3;
+        }
+      }
+    }
+    need -= above;
+    prefix = (prefix << 8) | (uint32_t)(255 - (4 * L + j));
+    if (c == need) break;  // the whole bin is taken: no tie inside it to resolve
   }
-  if (cnt_tau == 0) {  // tau stayed 0: every key qualifies
-#pragma unroll
-    for (int i = 0; i < NV; ++i) cnt_tau += __popcll(__ballot(lane + kWave * i < E));
-  }
-  // chosen: key > tau, plus the lowest-index keys == tau up to k in total
-  int above = 0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) above += __popcll(__ballot(key[i] > tau && lane + kWave * i < E));
-  int quota = k - above;
+  // chosen: (key >> shift) above prefix, plus the lowest-index `need` keys equal to it
+  int quota = need;
   uint64_t chosen[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const bool valid = lane + kWave * i < E;
-    const uint64_t eq = __ballot(valid && key[i] == tau);
+    const uint32_t kh = key[i] >> shift;
+    const uint64_t eq = __ballot(ok[i] && kh == prefix);
     const int my_rank = __popcll(eq & ((1ull << lane) - 1ull));
-    const bool pick = valid && (key[i] > tau || (key[i] == tau && my_rank < quota));
+    const bool pick = ok[i] && (kh > prefix || (kh == prefix && my_rank < quota));
     chosen[i] = __ballot(pick);
     quota -= __popcll(eq);
     quota = quota < 0 ? 0 : quota;
   }
-  (void)cnt_tau;
   // weights: exp(l - m) / sum over the chosen, m = the largest logit
   float lmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
     if ((chosen[i] >> lane) & 1ull) lmax = fmaxf(lmax, val[i]);
   const float m = wave_max(lmax);
-  float psum = 0.f, p[NV];
+  float psum = 0.f, pv[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    p[i] = ((chosen[i] >> lane) & 1ull) ? expf(val[i] - m) : 0.f;
-    psum += p[i];
+    pv[i] = ((chosen[i] >> lane) & 1ull) ? expf(val[i] - m) : 0.f;
+    psum += pv[i];
   }
   const float ps = group_sum<kWave>(psum);
   int base = 0;
@@ -186,24 +225,24 @@ __device__ __forceinline__ void select_set_nv(const float* lrow, int E, int k, i
     if ((chosen[i] >> lane) & 1ull) {
       const int pos = base + __popcll(chosen[i] & ((1ull << lane) - 1ull));
       ids_out[pos] = lane + kWave * i;
-      w_out[pos] = p[i] / ps;
+      w_out[pos] = pv[i] / ps;
     }
     base += __popcll(chosen[i]);
   }
 }
 
-__device__ __forceinline__ void select_set(const float* lrow, int E, int k, int lane, int* ids_out,
-                                           float* w_out) {
+__device__ __forceinline__ void select_set(const float* lrow, int E, int k, int lane, unsigned* hist,
+                                           int* ids_out, float* w_out) {
   if (E <= 64)
-    select_set_nv<1>(lrow, E, k, lane, ids_out, w_out);
+    select_set_nv<1>(lrow, E, k, lane, hist, ids_out, w_out);
   else if (E <= 128)
-    select_set_nv<2>(lrow, E, k, lane, ids_out, w_out);
+    select_set_nv<2>(lrow, E, k, lane, hist, ids_out, w_out);
   else if (E <= 256)
-    select_set_nv<4>(lrow, E, k, lane, ids_out, w_out);
+    select_set_nv<4>(lrow, E, k, lane, hist, ids_out, w_out);
   else if (E <= 512)
-    select_set_nv<8>(lrow, E, k, lane, ids_out, w_out);
+    select_set_nv<8>(lrow, E, k, lane, hist, ids_out, w_out);
   else
-    select_set_nv<16>(lrow, E, k, lane, ids_out, w_out);
+    select_set_nv<16>(lrow, E, k, lane, hist, ids_out, w_out);
 }
 
 }  // namespace moe

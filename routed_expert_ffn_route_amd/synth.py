@@ -229,10 +229,12 @@ def device_layer(T, H, E, k, I, I_shared, act=BF16, expert=BF16, shared=BF16, ou
         L.gate = torch.empty((E, I, H), device=device, dtype=torch.float32 if expert == F32 else torch.int16)
         L.up = torch.empty_like(L.gate)
         L.down = torch.empty((E, H, I), device=device, dtype=L.gate.dtype)
-        for e in range(E):
-            L.gate[e] = normal((I, H), 1.0 / math.sqrt(H), expert)
-            L.up[e] = normal((I, H), 1.0 / math.sqrt(H), expert)
-            L.down[e] = normal((H, I), 1.0 / math.sqrt(I), expert)
+        # experts in chunks of up to 16 (a few kernels per chunk, bounded fp32 temporaries)
+        for e0 in range(0, E, 16):
+            n = min(16, E - e0)
+            L.gate[e0:e0 + n] = normal((n, I, H), 1.0 / math.sqrt(H), expert)
+            L.up[e0:e0 + n] = normal((n, I, H), 1.0 / math.sqrt(H), expert)
+            L.down[e0:e0 + n] = normal((n, H, I), 1.0 / math.sqrt(I), expert)
     if I_shared > 0:
         L.sh_gate = normal((I_shared, H), 1.0 / math.sqrt(H), shared)
         L.sh_up = normal((I_shared, H), 1.0 / math.sqrt(H), shared)
