@@ -36,6 +36,7 @@ int check_shape(const moe_shape_t* s) {
   if (s->out_dtype != MOE_F32 && s->out_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
   if (s->T > kDecodeMaxT) {  // prefill path
     if (s->act_dtype != MOE_BF16 || s->expert_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+    if ((size_t)s->T * s->H * 2 >= ((size_t)1 << 31)) return MOE_EUNSUPPORTED;  // 32-bit row offsets
   }
   return MOE_OK;
 }

@@ -1,20 +1,24 @@
 // Prefill path (T > 16): the layer as grouped GEMMs on MFMA.
 //
 //  router   logits = x . Wr^T on bf16 MFMA: x is bf16 exactly and every fp32 router weight is
-//           split into three bf16 parts (hi + mid + lo == w), so each product is exact and the
-//           sum is accumulated in fp32 -- fp32-accurate logits at bf16 matrix-core rates.
+//           split into three bf16 parts (hi + mid + lo == w) by a small pass, so each product
+//           is exact and the three partial sums are added in fp32 -- fp32-accurate logits at
+//           bf16 matrix-core rates.
 //  select   one wave per token (descending rank, ties to the lower index).
 //  permute  histogram of assignments per expert -> prefix scan -> scatter of slots into expert
 //           groups -> block map of fixed-size row tiles ("Optimizing on-device inference for
 //           Apple Silicon", section "Keep expert routing on the GPU"; the shared expert is one
 //           more group holding every token).  No host synchronisation anywhere.
-//  gate/up  per tile: gather the tile's token rows of x, stream the group's gate and up rows
-//           through LDS, MFMA, SwiGLU in the epilogue, bf16 activations in grouped order
-//           (same page, sections "Decode weights during matrix multiplication" and "Match tile
-//           size to expert load").
+//  gate/up  per tile: the tile's token rows of x against the group's gate and up rows, SwiGLU
+//           in the epilogue, bf16 activations in grouped order (same page, sections "Decode
+//           weights during matrix multiplication" and "Match tile size to expert load").
 //  down     per tile: activations x Wd^T, scaled by the slot's routing weight in the
 //           epilogue, one bf16 row per slot.
 //  combine  y[t] = sum_j out[t*k + j] + out_shared[t], a fixed order (deterministic).
+//
+// All three GEMMs run one kernel, pf_gemm: 128 x 256 block tiles, K-steps of 32 staged in
+// a three-deep LDS ring that the buffer unit fills directly (loads to LDS, no register
+// staging), rows XOR-swizzled so that MFMA fragment reads are free of bank conflicts.
 #include "common.h"
 #include "kernels.h"
 #include "select.h"
@@ -24,11 +28,11 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kPfBM = 128;     // rows per tile (gate/up and down)
-constexpr int kPfBNI = 64;     // intermediate columns per gate/up block (x2: gate and up)
-constexpr int kPfBNH = 128;    // hidden columns per down block
-constexpr int kPfBK = 64;      // reduction step staged through LDS
-constexpr int kPfLDK = kPfBK + 8;  // padded LDS row (bf16 elements)
+constexpr int kPfBM = 128;     // rows per tile
+constexpr int kPfBN = 256;     // B rows per block (gate/up: 128 activation columns x 2)
+constexpr int kPfBK = 32;      // reduction step per LDS stage
+constexpr int kPfNS = 3;       // LDS ring depth
+constexpr int kPfStage = (kPfBM + kPfBN) * kPfBK * 2 / 16;  // 16-byte units per stage
 
 size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is) {
   const size_t S = (size_t)T * k, R = S + T;
@@ -36,7 +40,7 @@ size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is) {
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
   return up(sizeof(int) * (E + 2)) * 2 + up(sizeof(int) * R) +
          up(sizeof(int) * 2 * (size_t)prefill_tiles_cap(T, E, k)) + up(256) + up(2 * R * Imax) +
-         up(2 * R * (size_t)H);
+         up(2 * R * (size_t)H) + up(2 * 3 * (size_t)E * H);
 }
 
 // Upper bound of sum over the E+1 groups of ceil(rows / kPfBM).
@@ -54,6 +58,7 @@ struct PfLayout {
   int* ntiles;  // [1]
   uint16_t* act;  // [S+T][Imax]
   uint16_t* out;  // [S+T][H]
+  uint16_t* planes;  // [3][E][H] bf16 parts of the router weights
 };
 
 PfLayout pf_layout(const Args& A) {
@@ -75,11 +80,9 @@ PfLayout pf_layout(const Args& A) {
   L.act = (uint16_t*)b;
   b += up(2 * R * Imax);
   L.out = (uint16_t*)b;
+  b += up(2 * R * (size_t)A.H);
+  L.planes = (uint16_t*)b;
   return L;
-}
-
-__device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8_t, *(const uint4*)p);
 }
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -93,76 +96,244 @@ __device__ __forceinline__ int xcd_swizzle(int b, int nblocks) {
   return (b % 8) * per + b / 8;
 }
 
-// ------------------------------------------------------------------------------------------
-// Router: logits[T][E] = x . Wr^T (+ bias), Wr split into three bf16 parts on the fly.
-// Block: 64 tokens x 128 experts; 4 waves 2x2, wave tile 32 x 64 (two 32x32 MFMA tiles).
-// ------------------------------------------------------------------------------------------
-constexpr int kRtBT = 64, kRtBE = 128, kRtBK = 32, kRtLDK = kRtBK + 8;
+// Router weights -> three bf16 parts per element: hi = w truncated to bf16, mid = the
+// remainder truncated, lo = what is left rounded (it fits exactly); hi + mid + lo == w.
+__global__ __launch_bounds__(256) void pf_split_router(Args A, uint16_t* planes) {
+  const size_t n = (size_t)A.E * A.H;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n / 4; i += (size_t)gridDim.x * 256) {
+    const float4 w = ((const float4*)A.rw)[i];
+    const float wv[4] = {w.x, w.y, w.z, w.w};
+    uint16_t hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t uh = __float_as_uint(wv[j]) & 0xffff0000u;
+      const float r1 = wv[j] - __uint_as_float(uh);
+      const uint32_t um = __float_as_uint(r1) & 0xffff0000u;
+      const float r2 = r1 - __uint_as_float(um);
+      hi[j] = (uint16_t)(uh >> 16);
+      mid[j] = (uint16_t)(um >> 16);
+      lo[j] = f32_to_bf16(r2);
+    }
+    auto pack = [](const uint16_t* v) {
+      return make_uint2(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16);
+    };
+    ((uint2*)planes)[i] = pack(hi);
+    ((uint2*)(planes + n))[i] = pack(mid);
+    ((uint2*)(planes + 2 * n))[i] = pack(lo);
+  }
+}
 
-__global__ __launch_bounds__(256) void pf_router(Args A) {
-  __shared__ __attribute__((aligned(16))) uint16_t sx[kRtBT * kRtLDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sw[3][kRtBE * kRtLDK];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// ------------------------------------------------------------------------------------------
+// Grouped GEMM.  A block computes a 128-row x 256-column tile of C = A . B^T (B rows are
+// output columns, K contiguous); four waves in a 2 x 2 grid own 64 x 128 each (2 x 4 MFMA
+// 32x32x16 tiles).  Operands are read through buffer resources: an offset at or past a
+// resource's size reads as zero (kOOB), which masks rows past the tile or matrix end.
+// Each K-step of 32 lands in one of three LDS stages via buffer loads to LDS (every lane
+// writes its 16 bytes at stage base + 16 * lane); 16-byte chunk c of row r sits at unit
+// r * 4 + (c ^ ((r >> 1) & 3)), which spreads the eight rows read together over distinct
+// banks.  Step s + 2 is requested before step s is multiplied: one barrier per step.
+//
+// MODE 0 gate/up: A = gathered token rows of x; B rows per wave column half wn are, in 32-row
+//        groups, gate / up / gate / up of the activation columns n0 + 64 wn ... + 63; the
+//        epilogue applies SwiGLU in registers and stores bf16 activations.
+// MODE 1 down: A = activation rows of the tile; B = Wd rows n0 ...; the epilogue scales by
+//        the slot's routing weight and stores bf16 at the slot's row.
+// MODE 2 router: A = token rows t0 ...; B rows per wave column half are the hi / mid / lo
+//        parts of experts e0 + 32 wn ... (fourth group unused); the epilogue adds the three.
+// ------------------------------------------------------------------------------------------
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource: base address, stride 0, size in bytes (capped below kOOB), format word.
+__device__ __forceinline__ i32x4_t buf_rsrc(const void* base, size_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return i32x4_t{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff,
+                 (int)(bytes < (size_t)kOOB ? bytes : (size_t)kOOB - 1), kBufWord3};
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at lds_off + 16 * lane.  Written as
+// inline assembly so that the compiler does not treat the pending write to LDS as a reason to
+// wait for every outstanding load before each LDS read: the waits are placed by hand.
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_off)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)p;
+}
+
+__device__ __forceinline__ int swz_unit(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 3)); }
+
+// s_waitcnt with only the vector-memory count constrained (expcnt and lgkmcnt left at max)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks) {
+  // one LDS object per stage, so that waits for the loads into one stage do not cover reads
+  // of another
+  __shared__ __attribute__((aligned(16))) uint4 sm0[kPfStage];
+  __shared__ __attribute__((aligned(16))) uint4 sm1[kPfStage];
+  __shared__ __attribute__((aligned(16))) uint4 sm2[kPfStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int t0 = blockIdx.x * kRtBT, e0 = blockIdx.y * kRtBE;
-  f32x16_t acc[2] = {};
-  // loaders: x tile 64 rows x 32 k = 256 chunks of 8 bf16 (one per thread);
-  // Wr tile 128 rows x 32 k fp32 = 1024 chunks of 4 floats (four per thread)
-  const int xr = tid >> 2, xc = tid & 3;
-  const bool xok = t0 + xr < A.T;
-  const uint16_t* xp = (const uint16_t*)A.x + (size_t)(xok ? t0 + xr : 0) * A.H + xc * 8;
-  for (int k0 = 0; k0 < A.H; k0 += kRtBK) {
-    uint4 xv = xok ? *(const uint4*)(xp + k0) : make_uint4(0, 0, 0, 0);
-    *(uint4*)&sx[xr * kRtLDK + xc * 8] = xv;
+  const int b = xcd_swizzle(blockIdx.x, nblocks);
+  const int ti = b / nb_per_tile, nb = b - ti * nb_per_tile;
+  const int S = A.T * A.k;
+  const size_t Imax = A.I > A.Is ? A.I : A.Is;
+
+  // ---- the tile
+  int nrows, pos0 = 0, g = 0, K, N;
+  if constexpr (MODE == 2) {
+    nrows = min(kPfBM, A.T - ti * kPfBM);
+    K = A.H;
+    N = A.E;
+  } else {
+    if (ti >= *L.ntiles) return;
+    g = L.tiles[2 * ti];
+    const int it = L.tiles[2 * ti + 1];
+    nrows = min(kPfBM, L.count[g] - it * kPfBM);
+    pos0 = L.offset[g] + it * kPfBM;
+    K = MODE == 0 ? A.H : (g == A.E ? A.Is : A.I);
+    N = MODE == 0 ? (g == A.E ? A.Is : A.I) : A.H;
+  }
+  const int n0 = MODE == 0 ? nb * (kPfBN / 2) : MODE == 1 ? nb * kPfBN : nb * 64;
+  if (n0 >= N) return;
+
+  // ---- per-lane load slots: 2 A and 4 B 16-byte chunks per K-step
+  i32x4_t ra, rb[4];
+  uint32_t ao[2], bo[4];
+  if constexpr (MODE == 0) ra = buf_rsrc(A.x, (size_t)A.T * A.H * 2);
+  if constexpr (MODE == 1) ra = buf_rsrc(L.act + (size_t)pos0 * Imax, (size_t)nrows * Imax * 2);
+  if constexpr (MODE == 2) ra = buf_rsrc((const uint16_t*)A.x + (size_t)ti * kPfBM * A.H, (size_t)nrows * A.H * 2);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = tid + 256 * q, r = c >> 3, kc = c & 7;
-      const bool ok = e0 + r < A.E;
-      float4 w = ok ? *(const float4*)(A.rw + (size_t)(e0 + r) * A.H + k0 + kc * 4) : make_float4(0, 0, 0, 0);
-      float wv[4] = {w.x, w.y, w.z, w.w};
-      uint16_t hi[4], mid[4], lo[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t u = __float_as_uint(wv[j]);
-        const uint32_t uh = u & 0xffff0000u;               // truncation: exact leading part
-        const float r1 = wv[j] - __uint_as_float(uh);       // exact remainder
-        const uint32_t um = __float_as_uint(r1) & 0xffff0000u;
-        const float r2 = r1 - __uint_as_float(um);          // exact; fits in bf16
-        hi[j] = (uint16_t)(uh >> 16);
-        mid[j] = (uint16_t)(um >> 16);
-        lo[j] = f32_to_bf16(r2);
-      }
-      uint2 vh = make_uint2(hi[0] | (uint32_t)hi[1] << 16, hi[2] | (uint32_t)hi[3] << 16);
-      uint2 vm = make_uint2(mid[0] | (uint32_t)mid[1] << 16, mid[2] | (uint32_t)mid[3] << 16);
-      uint2 vl = make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
-      *(uint2*)&sw[0][r * kRtLDK + kc * 4] = vh;
-      *(uint2*)&sw[1][r * kRtLDK + kc * 4] = vm;
-      *(uint2*)&sw[2][r * kRtLDK + kc * 4] = vl;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < kRtBK; ks += 16) {
-      const int kk = ks + (lane >> 5) * 8;
-      const bf16x8_t a = lds_frag(&sx[(wm * 32 + (lane & 31)) * kRtLDK + kk]);
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int er = wn * 64 + n * 32 + (lane & 31);
-#pragma unroll
-        for (int p = 0; p < 3; ++p) acc[n] = mfma32(a, lds_frag(&sw[p][er * kRtLDK + kk]), acc[n]);
+  for (int j = 0; j < 2; ++j) {
+    const int p = (wave * 2 + j) * 64 + lane, r = p >> 2, c = (p & 3) ^ ((r >> 1) & 3);
+    uint32_t rowb = kOOB;
+    if (r < nrows) {
+      if constexpr (MODE == 0) {
+        const int slot = L.rows[pos0 + r];
+        const int t = slot < S ? slot / A.k : slot - S;
+        rowb = (uint32_t)t * A.H * 2u;
+      } else if constexpr (MODE == 1) {
+        rowb = (uint32_t)r * (uint32_t)Imax * 2u;
+      } else {
+        rowb = (uint32_t)r * A.H * 2u;
       }
     }
-    __syncthreads();
+    ao[j] = rowb == kOOB ? kOOB : rowb + c * 16u;
   }
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int e = e0 + wn * 64 + n * 32 + (lane & 31);
+  for (int j = 0; j < 4; ++j) {
+    // instruction j of this wave covers B rows 16 (4 wave + j) ... + 15
+    const int p = (wave * 4 + j) * 64 + lane, r = p >> 2, c = (p & 3) ^ ((r >> 1) & 3);
+    const int half = r >> 7, jj = r & 127;
+    uint32_t rowb = kOOB;
+    if constexpr (MODE == 0) {
+      const bool up = (jj >> 5) & 1;  // uniform per instruction
+      const bool sh = g == A.E;
+      const uint16_t* base = up ? (sh ? (const uint16_t*)A.sup : (const uint16_t*)A.up + (size_t)g * A.I * A.H)
+                                : (sh ? (const uint16_t*)A.sgate : (const uint16_t*)A.gate + (size_t)g * A.I * A.H);
+      rb[j] = buf_rsrc(base, (size_t)N * A.H * 2);
+      const int col = n0 + half * 64 + (jj >> 6) * 32 + (jj & 31);
+      if (col < N) rowb = (uint32_t)col * A.H * 2u;
+    } else if constexpr (MODE == 1) {
+      const uint16_t* base = g == A.E ? (const uint16_t*)A.sdown : (const uint16_t*)A.down + (size_t)g * A.H * A.I;
+      rb[j] = buf_rsrc(base, (size_t)A.H * K * 2);
+      const int h = n0 + r;
+      if (h < A.H) rowb = (uint32_t)h * K * 2u;
+    } else {
+      rb[j] = buf_rsrc(L.planes, (size_t)3 * A.E * A.H * 2);
+      const int plane = jj >> 5, e = n0 + half * 32 + (jj & 31);
+      if (plane < 3 && e < A.E) rowb = ((uint32_t)plane * A.E + e) * A.H * 2u;
+    }
+    bo[j] = rowb == kOOB ? kOOB : rowb + c * 16u;
+  }
+
+  const int nk = K / kPfBK;
+  auto issue = [&](int st, uint4* stage) {
+    const uint32_t kb = (uint32_t)(st < nk ? st : nk - 1) * kPfBK * 2u;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(ra, ao[j] + kb, lds_addr(stage + (wave * 2 + j) * 64));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(rb[j], bo[j] + kb, lds_addr(stage + kPfBM * 4 + (wave * 4 + j) * 64));
+  };
+
+  // rows of this wave that hold data (uniform): skip MFMA tiles wholly past the tile end
+  const int mlive = min(2, max(0, (nrows - wm * 64 + 31) / 32));
+  f32x16_t acc[2][4] = {};
+  auto step = [&](int s, const uint4* st, uint4* next) {
+    wait_vm<6>();      // this wave's loads of step s have landed (step s + 1 may be in flight)
+    __syncthreads();   // ... and every other wave's; all are done with step s - 1's stage
+    issue(s + 2, next);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      bf16x8_t af[2], bfr[4];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        af[m] = __builtin_bit_cast(bf16x8_t, st[swz_unit(wm * 64 + m * 32 + (lane & 31), c)]);
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        bfr[n] = __builtin_bit_cast(bf16x8_t, st[kPfBM * 4 + swz_unit(wn * 128 + n * 32 + (lane & 31), c)]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (m >= mlive) break;  // uniform
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[m][n] = mfma32(af[m], bfr[n], acc[m][n]);
+      }
+    }
+  };
+  issue(0, sm0);
+  issue(1, sm1);
+  for (int s = 0; s < nk; s += 3) {
+    step(s, sm0, sm2);
+    if (s + 1 >= nk) break;
+    step(s + 1, sm1, sm0);
+    if (s + 2 >= nk) break;
+    step(s + 2, sm2, sm1);
+  }
+  wait_vm<0>();  // no load may still write this block's LDS after it retires
+
+  // ---- epilogue; C row = wm * 64 + m * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int t = t0 + wm * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
-      if (t < A.T && e < A.E) {
-        float l = acc[n][r];
-        if (A.rbias) l += A.rbias[(size_t)t * A.bias_stride + e];
-        A.logits[(size_t)t * A.E + e] = l;
+      const int row = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+      if (row >= nrows) continue;
+      if constexpr (MODE == 0) {
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const int col = n0 + wn * 64 + pr * 32 + (lane & 31);
+          if (col < N)
+            L.act[(size_t)(pos0 + row) * Imax + col] = f32_to_bf16(silu(acc[m][2 * pr][r]) * acc[m][2 * pr + 1][r]);
+        }
+      } else if constexpr (MODE == 1) {
+        const int slot = L.rows[pos0 + row];
+        const float w = slot < S ? A.cw[slot] : 1.f;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int h = n0 + wn * 128 + n * 32 + (lane & 31);
+          if (h < A.H) L.out[(size_t)slot * A.H + h] = f32_to_bf16(w * acc[m][n][r]);
+        }
+      } else {
+        const int e = n0 + wn * 32 + (lane & 31), t = ti * kPfBM + row;
+        if (e < A.E) {
+          float l = (acc[m][0][r] + acc[m][1][r]) + acc[m][2][r];
+          if (A.rbias) l += A.rbias[(size_t)t * A.bias_stride + e];
+          A.logits[(size_t)t * A.E + e] = l;
+        }
       }
     }
   }
@@ -181,202 +352,6 @@ __global__ __launch_bounds__(256) void pf_select(Args A) {
   if (A.o_ids && lane < A.k) {  // each lane re-reads only what it wrote itself
     A.o_ids[(size_t)t * A.k + lane] = ids[lane];
     A.o_w[(size_t)t * A.k + lane] = w[lane];
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// Grouped GEMM main loop shared by gate/up and down.  A block stages a 128-row A tile and a
-// 128-row B tile (rows = output columns, K contiguous) per K-step of 64 through two LDS
-// buffers, with the next step's global loads held in registers: one barrier per step.  Each
-// thread loads four 16-byte chunks of A and four of B per step; every load is unconditional
-// (clamped to a valid address) and masked by selecting zero, so nothing branches in the loop.
-// Four waves in a 2x2 grid each own a 64 x 64 corner = 2 x 2 MFMA 32x32 tiles.
-// ------------------------------------------------------------------------------------------
-struct TileOperands {
-  const uint16_t* ap[4];  // A row chunk pointers (clamped)
-  const uint16_t* bp[4];  // B row chunk pointers (clamped)
-  bool aok[4], bok[4];    // row validity
-  int K;                  // reduction length (multiple of 32)
-};
-
-__device__ __forceinline__ uint4 sel4(bool ok, uint4 v) {
-  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
-}
-
-__device__ __forceinline__ void tile_load(const TileOperands& op, int k0, int kc, uint4* ra, uint4* rb) {
-  const bool kok = k0 + kc * 8 < op.K;
-  const int ko = kok ? k0 : 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    ra[q] = sel4(kok && op.aok[q], *(const uint4*)(op.ap[q] + ko));
-    rb[q] = sel4(kok && op.bok[q], *(const uint4*)(op.bp[q] + ko));
-  }
-}
-
-__device__ __forceinline__ void tile_store(uint16_t* sa, uint16_t* sb, int tid, const uint4* ra,
-                                           const uint4* rb) {
-  const int kc = tid & 7;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = (tid >> 3) + 32 * q;
-    *(uint4*)&sa[r * kPfLDK + kc * 8] = ra[q];
-    *(uint4*)&sb[r * kPfLDK + kc * 8] = rb[q];
-  }
-}
-
-__device__ __forceinline__ void tile_mma(const uint16_t* sa, const uint16_t* sb, int lane, int wm, int wn,
-                                         f32x16_t (&acc)[2][2]) {
-#pragma unroll
-  for (int ks = 0; ks < kPfBK; ks += 16) {
-    const int kk = ks + (lane >> 5) * 8;
-    bf16x8_t af[2], bfr[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) af[m] = lds_frag(&sa[(wm * 64 + m * 32 + (lane & 31)) * kPfLDK + kk]);
-#pragma unroll
-    for (int n = 0; n < 2; ++n) bfr[n] = lds_frag(&sb[(wn * 64 + n * 32 + (lane & 31)) * kPfLDK + kk]);
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int n = 0; n < 2; ++n) acc[m][n] = mfma32(af[m], bfr[n], acc[m][n]);
-  }
-}
-
-__device__ __forceinline__ void tile_gemm(const TileOperands& op, uint16_t (*sa)[kPfBM * kPfLDK],
-                                          uint16_t (*sb)[kPfBM * kPfLDK], f32x16_t (&acc)[2][2]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, kc = tid & 7;
-  const int nk = (op.K + kPfBK - 1) / kPfBK;
-  uint4 r0a[4], r0b[4], r1a[4], r1b[4];
-  tile_load(op, 0, kc, r0a, r0b);
-  tile_load(op, kPfBK, kc, r1a, r1b);
-  tile_store(sa[0], sb[0], tid, r0a, r0b);
-  for (int kt = 0; kt < nk; kt += 2) {
-    __syncthreads();
-    if (kt + 1 < nk) tile_store(sa[1], sb[1], tid, r1a, r1b);
-    if (kt + 2 < nk) tile_load(op, (kt + 2) * kPfBK, kc, r0a, r0b);
-    tile_mma(sa[0], sb[0], lane, wm, wn, acc);
-    if (kt + 1 < nk) {
-      __syncthreads();
-      if (kt + 2 < nk) tile_store(sa[0], sb[0], tid, r0a, r0b);
-      if (kt + 3 < nk) tile_load(op, (kt + 3) * kPfBK, kc, r1a, r1b);
-      tile_mma(sa[1], sb[1], lane, wm, wn, acc);
-    }
-  }
-}
-
-// Gate/up: block = (tile, 64 intermediate columns).  B rows 0..63 are gate rows n0..n0+63,
-// rows 64..127 the matching up rows, so wave column half wn=0 holds gate and wn=1 holds up
-// for the same 64 columns -> exchanged through LDS for the SwiGLU epilogue.
-__global__ __launch_bounds__(256, 2) void pf_gateup(Args A, PfLayout L, int nb_per_tile, int nblocks) {
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][kPfBM * kPfLDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][kPfBM * kPfLDK];
-  const int b = xcd_swizzle(blockIdx.x, nblocks);
-  const int ti = b / nb_per_tile, nb = b - ti * nb_per_tile;
-  if (ti >= *L.ntiles) return;
-  const int g = L.tiles[2 * ti], it = L.tiles[2 * ti + 1];
-  const bool shared = g == A.E;
-  const int N = shared ? A.Is : A.I;
-  const int n0 = nb * kPfBNI;
-  if (n0 >= N) return;
-  const int r0 = it * kPfBM, nrows = min(kPfBM, L.count[g] - r0);
-  const int pos0 = L.offset[g] + r0;
-  const int S = A.T * A.k;
-  const size_t Imax = A.I > A.Is ? A.I : A.Is;
-  const uint16_t* wg = shared ? (const uint16_t*)A.sgate : (const uint16_t*)A.gate + (size_t)g * A.I * A.H;
-  const uint16_t* wu = shared ? (const uint16_t*)A.sup : (const uint16_t*)A.up + (size_t)g * A.I * A.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, kc = tid & 7;
-  TileOperands op;
-  op.K = A.H;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = (tid >> 3) + 32 * q;
-    op.aok[q] = r < nrows;
-    const int slot = L.rows[pos0 + (op.aok[q] ? r : 0)];
-    const int t = slot < S ? slot / A.k : slot - S;
-    op.ap[q] = (const uint16_t*)A.x + (size_t)t * A.H + kc * 8;
-    const int n = n0 + (r & 63);
-    op.bok[q] = n < N;
-    op.bp[q] = (r < 64 ? wg : wu) + (size_t)(op.bok[q] ? n : 0) * A.H + kc * 8;
-  }
-  f32x16_t acc[2][2] = {};
-  tile_gemm(op, sa, sb, acc);
-  // SwiGLU epilogue: the wn=1 waves (up) hand their tiles to the wn=0 waves (gate) via LDS
-  __syncthreads();
-  // [wm][m][n][r][lane]: consecutive lanes hit consecutive banks
-  float* xch = (float*)&sa[0][0];  // 2 x 64 floats x 64 lanes = 32 KB (fits in sa)
-  if (wn == 1) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) xch[(((wm * 2 + m) * 2 + n) * 16 + r) * 64 + lane] = acc[m][n][r];
-  }
-  __syncthreads();
-  if (wn == 0) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int col = n0 + n * 32 + (lane & 31);
-        if (col >= N) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
-          const float up = xch[(((wm * 2 + m) * 2 + n) * 16 + r) * 64 + lane];
-          if (row < nrows) L.act[(size_t)(pos0 + row) * Imax + col] = f32_to_bf16(silu(acc[m][n][r]) * up);
-        }
-      }
-    }
-  }
-}
-
-// Down: block = (tile, 128 hidden columns).  Each row's result is scaled by its slot's
-// routing weight (shared expert: 1) and stored as bf16 at its slot index.
-__global__ __launch_bounds__(256, 2) void pf_down(Args A, PfLayout L, int nb_per_tile, int nblocks) {
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][kPfBM * kPfLDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][kPfBM * kPfLDK];
-  const int b = xcd_swizzle(blockIdx.x, nblocks);
-  const int ti = b / nb_per_tile, nb = b - ti * nb_per_tile;
-  if (ti >= *L.ntiles) return;
-  const int g = L.tiles[2 * ti], it = L.tiles[2 * ti + 1];
-  const bool shared = g == A.E;
-  const int h0 = nb * kPfBNH;
-  const int r0 = it * kPfBM, nrows = min(kPfBM, L.count[g] - r0);
-  const int pos0 = L.offset[g] + r0;
-  const size_t Imax = A.I > A.Is ? A.I : A.Is;
-  const uint16_t* wd = shared ? (const uint16_t*)A.sdown : (const uint16_t*)A.down + (size_t)g * A.H * A.I;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, kc = tid & 7;
-  TileOperands op;
-  op.K = shared ? A.Is : A.I;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = (tid >> 3) + 32 * q;
-    op.aok[q] = r < nrows;
-    op.ap[q] = L.act + (size_t)(pos0 + (op.aok[q] ? r : 0)) * Imax + kc * 8;
-    const int h = h0 + r;
-    op.bok[q] = h < A.H;
-    op.bp[q] = wd + (size_t)(op.bok[q] ? h : 0) * op.K + kc * 8;
-  }
-  f32x16_t acc[2][2] = {};
-  tile_gemm(op, sa, sb, acc);
-  const int S = A.T * A.k;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
-      if (row >= nrows) continue;
-      const int slot = L.rows[pos0 + row];
-      const float w = slot < S ? A.cw[slot] : 1.f;
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int h = h0 + wn * 64 + n * 32 + (lane & 31);
-        if (h < A.H) L.out[(size_t)slot * A.H + h] = f32_to_bf16(w * acc[m][n][r]);
-      }
-    }
   }
 }
 
@@ -422,8 +397,12 @@ __global__ __launch_bounds__(1024) void permute(const int* ids, int T, int k, in
 int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook) {
   hipError_t err;
   if (!A.logits_in) {
+    const PfLayout L = pf_layout(A);
     hook.pre("pf_router", st);
-    pf_router<<<dim3((A.T + kRtBT - 1) / kRtBT, (A.E + kRtBE - 1) / kRtBE), 256, 0, st>>>(A);
+    pf_split_router<<<256, 256, 0, st>>>(A, L.planes);
+    const int nbt = (A.E + 63) / 64, tiles = (A.T + kPfBM - 1) / kPfBM;
+    const int nblocks = (tiles * nbt + 7) / 8 * 8;
+    pf_gemm<2><<<nblocks, 256, 0, st>>>(A, L, nbt, nblocks);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   }
@@ -447,18 +426,18 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   const int cap = prefill_tiles_cap(A.T, A.E, A.k);
   const int Imax = A.I > A.Is ? A.I : A.Is;
   {
-    const int nbt = (Imax + kPfBNI - 1) / kPfBNI;
+    const int nbt = (Imax + kPfBN / 2 - 1) / (kPfBN / 2);
     const int nblocks = (cap * nbt + 7) / 8 * 8;
     hook.pre("pf_gateup", st);
-    pf_gateup<<<nblocks, 256, 0, st>>>(A, L, nbt, nblocks);
+    pf_gemm<0><<<nblocks, 256, 0, st>>>(A, L, nbt, nblocks);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   }
   {
-    const int nbt = (A.H + kPfBNH - 1) / kPfBNH;
+    const int nbt = (A.H + kPfBN - 1) / kPfBN;
     const int nblocks = (cap * nbt + 7) / 8 * 8;
     hook.pre("pf_down", st);
-    pf_down<<<nblocks, 256, 0, st>>>(A, L, nbt, nblocks);
+    pf_gemm<1><<<nblocks, 256, 0, st>>>(A, L, nbt, nblocks);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   }
