@@ -31,8 +31,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kPfBM = 128;     // rows per tile
 constexpr int kPfBN = 256;     // B rows per block (gate/up: 128 activation columns x 2)
 constexpr int kPfBK = 32;      // reduction step per LDS stage
-constexpr int kPfNS = 3;       // LDS ring depth
-constexpr int kPfStage = (kPfBM + kPfBN) * kPfBK * 2 / 16;  // 16-byte units per stage
+constexpr int kPfNS = 3;       // LDS ring depth (two 256-thread blocks per CU)
 
 size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is) {
   const size_t S = (size_t)T * k, R = S + T;
@@ -124,14 +123,16 @@ __global__ __launch_bounds__(256) void pf_split_router(Args A, uint16_t* planes)
 }
 
 // ------------------------------------------------------------------------------------------
-// Grouped GEMM.  A block computes a 128-row x 256-column tile of C = A . B^T (B rows are
-// output columns, K contiguous); four waves in a 2 x 2 grid own 64 x 128 each (2 x 4 MFMA
-// 32x32x16 tiles).  Operands are read through buffer resources: an offset at or past a
+// Grouped GEMM.  A block computes a BM-row x 256-column tile of C = A . B^T (B rows are
+// output columns, K contiguous); BM / 32 waves in a (BM / 64) x 2 grid own 64 x 128 each
+// (2 x 4 MFMA 32x32x16 tiles).  Operands are read through buffer resources: an offset at or past a
 // resource's size reads as zero (kOOB), which masks rows past the tile or matrix end.
-// Each K-step of 32 lands in one of three LDS stages via buffer loads to LDS (every lane
+// Each K-step of 32 lands in one of NS LDS stages via buffer loads to LDS (every lane
 // writes its 16 bytes at stage base + 16 * lane); 16-byte chunk c of row r sits at unit
-// r * 4 + (c ^ ((r >> 1) & 3)), which spreads the eight rows read together over distinct
-// banks.  Step s + 2 is requested before step s is multiplied: one barrier per step.
+// r * 4 + (c ^ (((r >> 1) ^ (r >> 2)) & 3)), which puts any 16 consecutive rows' copies of
+// one chunk in distinct 16-byte bank slots of a 256-byte bank row (and any 8 in a 128-byte
+// one), so fragment reads are free of bank conflicts.  Step s + NS - 1 is requested before
+// step s is multiplied: one barrier per step.
 //
 // MODE 0 gate/up: A = gathered token rows of x; B rows per wave column half wn are, in 32-row
 //        groups, gate / up / gate / up of the activation columns n0 + 64 wn ... + 63; the
@@ -168,7 +169,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_t*)p;
 }
 
-__device__ __forceinline__ int swz_unit(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 3)); }
+__device__ __forceinline__ int swz_unit(int r, int c) { return r * 4 + (c ^ (((r >> 1) ^ (r >> 2)) & 3)); }
 
 // s_waitcnt with only the vector-memory count constrained (expcnt and lgkmcnt left at max)
 template <int N>
@@ -177,13 +178,11 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256, 2) void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks) {
-  // one LDS object per stage, so that waits for the loads into one stage do not cover reads
-  // of another
-  __shared__ __attribute__((aligned(16))) uint4 sm0[kPfStage];
-  __shared__ __attribute__((aligned(16))) uint4 sm1[kPfStage];
-  __shared__ __attribute__((aligned(16))) uint4 sm2[kPfStage];
+template <int MODE, int BM, int NS>
+__global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks) {
+  constexpr int kStage = (BM + kPfBN) * kPfBK * 2 / 16;  // 16-byte units per stage
+  constexpr int kNB = 512 / BM;                           // B load instructions per wave per step
+  __shared__ __attribute__((aligned(16))) uint4 smem[NS * kStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -195,15 +194,15 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(Args A, PfLayout L, int nb_per
   // ---- the tile
   int nrows, pos0 = 0, g = 0, K, N;
   if constexpr (MODE == 2) {
-    nrows = min(kPfBM, A.T - ti * kPfBM);
+    nrows = min(BM, A.T - ti * BM);
     K = A.H;
     N = A.E;
   } else {
     if (ti >= *L.ntiles) return;
     g = L.tiles[2 * ti];
     const int it = L.tiles[2 * ti + 1];
-    nrows = min(kPfBM, L.count[g] - it * kPfBM);
-    pos0 = L.offset[g] + it * kPfBM;
+    nrows = min(BM, L.count[g] - it * BM);
+    pos0 = L.offset[g] + it * BM;
     K = MODE == 0 ? A.H : (g == A.E ? A.Is : A.I);
     N = MODE == 0 ? (g == A.E ? A.Is : A.I) : A.H;
   }
@@ -211,14 +210,14 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(Args A, PfLayout L, int nb_per
   if (n0 >= N) return;
 
   // ---- per-lane load slots: 2 A and 4 B 16-byte chunks per K-step
-  i32x4_t ra, rb[4];
-  uint32_t ao[2], bo[4];
+  i32x4_t ra, rb[kNB];
+  uint32_t ao[2], bo[kNB];
   if constexpr (MODE == 0) ra = buf_rsrc(A.x, (size_t)A.T * A.H * 2);
   if constexpr (MODE == 1) ra = buf_rsrc(L.act + (size_t)pos0 * Imax, (size_t)nrows * Imax * 2);
-  if constexpr (MODE == 2) ra = buf_rsrc((const uint16_t*)A.x + (size_t)ti * kPfBM * A.H, (size_t)nrows * A.H * 2);
+  if constexpr (MODE == 2) ra = buf_rsrc((const uint16_t*)A.x + (size_t)ti * BM * A.H, (size_t)nrows * A.H * 2);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int p = (wave * 2 + j) * 64 + lane, r = p >> 2, c = (p & 3) ^ ((r >> 1) & 3);
+    const int p = (wave * 2 + j) * 64 + lane, r = p >> 2, c = (p & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
     uint32_t rowb = kOOB;
     if (r < nrows) {
       if constexpr (MODE == 0) {
@@ -234,9 +233,9 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(Args A, PfLayout L, int nb_per
     ao[j] = rowb == kOOB ? kOOB : rowb + c * 16u;
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // instruction j of this wave covers B rows 16 (4 wave + j) ... + 15
-    const int p = (wave * 4 + j) * 64 + lane, r = p >> 2, c = (p & 3) ^ ((r >> 1) & 3);
+  for (int j = 0; j < kNB; ++j) {
+    // instruction j of this wave covers B rows 16 (kNB wave + j) ... + 15
+    const int p = (wave * kNB + j) * 64 + lane, r = p >> 2, c = (p & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
     const int half = r >> 7, jj = r & 127;
     uint32_t rowb = kOOB;
     if constexpr (MODE == 0) {
@@ -266,16 +265,34 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(Args A, PfLayout L, int nb_per
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(ra, ao[j] + kb, lds_addr(stage + (wave * 2 + j) * 64));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(rb[j], bo[j] + kb, lds_addr(stage + kPfBM * 4 + (wave * 4 + j) * 64));
+    for (int j = 0; j < kNB; ++j) dma16(rb[j], bo[j] + kb, lds_addr(stage + BM * 4 + (wave * kNB + j) * 64));
   };
+
+  // down: the tile's slots and routing weights, staged in LDS while the operands stream
+  __shared__ int s_slot[BM];
+  __shared__ float s_wt[BM];
+  if constexpr (MODE == 1) {
+    if (tid < nrows) {
+      const int slot = L.rows[pos0 + tid];
+      s_slot[tid] = slot;
+      s_wt[tid] = slot < S ? A.cw[slot] : 1.f;
+    }
+  }
+  // router: this lane's bias column when the bias is shared by all tokens
+  float bias_e = 0.f;
+  if constexpr (MODE == 2) {
+    const int e = n0 + wn * 32 + (lane & 31);
+    if (A.rbias && A.bias_stride == 0 && e < A.E) bias_e = A.rbias[e];
+  }
 
   // rows of this wave that hold data (uniform): skip MFMA tiles wholly past the tile end
   const int mlive = min(2, max(0, (nrows - wm * 64 + 31) / 32));
   f32x16_t acc[2][4] = {};
-  auto step = [&](int s, const uint4* st, uint4* next) {
-    wait_vm<6>();      // this wave's loads of step s have landed (step s + 1 may be in flight)
-    __syncthreads();   // ... and every other wave's; all are done with step s - 1's stage
-    issue(s + 2, next);
+  auto step = [&](int s) {
+    wait_vm<(2 + kNB) * (NS - 2)>();  // this wave's loads of step s have landed (later ones in flight)
+    __syncthreads();          // ... and every other wave's; all are done with step s - 1's stage
+    issue(s + NS - 1, smem + ((s + NS - 1) % NS) * kStage);
+    const uint4* st = smem + (s % NS) * kStage;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int c = ks * 2 + (lane >> 5);
@@ -285,7 +302,7 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(Args A, PfLayout L, int nb_per
         af[m] = __builtin_bit_cast(bf16x8_t, st[swz_unit(wm * 64 + m * 32 + (lane & 31), c)]);
 #pragma unroll
       for (int n = 0; n < 4; ++n)
-        bfr[n] = __builtin_bit_cast(bf16x8_t, st[kPfBM * 4 + swz_unit(wn * 128 + n * 32 + (lane & 31), c)]);
+        bfr[n] = __builtin_bit_cast(bf16x8_t, st[BM * 4 + swz_unit(wn * 128 + n * 32 + (lane & 31), c)]);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         if (m >= mlive) break;  // uniform
@@ -294,15 +311,9 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(Args A, PfLayout L, int nb_per
       }
     }
   };
-  issue(0, sm0);
-  issue(1, sm1);
-  for (int s = 0; s < nk; s += 3) {
-    step(s, sm0, sm2);
-    if (s + 1 >= nk) break;
-    step(s + 1, sm1, sm0);
-    if (s + 2 >= nk) break;
-    step(s + 2, sm2, sm1);
-  }
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) issue(i, smem + i * kStage);
+  for (int s = 0; s < nk; ++s) step(s);
   wait_vm<0>();  // no load may still write this block's LDS after it retires
 
   // ---- epilogue; C row = wm * 64 + m * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4
@@ -320,18 +331,18 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(Args A, PfLayout L, int nb_per
             L.act[(size_t)(pos0 + row) * Imax + col] = f32_to_bf16(silu(acc[m][2 * pr][r]) * acc[m][2 * pr + 1][r]);
         }
       } else if constexpr (MODE == 1) {
-        const int slot = L.rows[pos0 + row];
-        const float w = slot < S ? A.cw[slot] : 1.f;
+        const int slot = s_slot[row];
+        const float w = s_wt[row];
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
           const int h = n0 + wn * 128 + n * 32 + (lane & 31);
           if (h < A.H) L.out[(size_t)slot * A.H + h] = f32_to_bf16(w * acc[m][n][r]);
         }
       } else {
-        const int e = n0 + wn * 32 + (lane & 31), t = ti * kPfBM + row;
+        const int e = n0 + wn * 32 + (lane & 31), t = ti * BM + row;
         if (e < A.E) {
           float l = (acc[m][0][r] + acc[m][1][r]) + acc[m][2][r];
-          if (A.rbias) l += A.rbias[(size_t)t * A.bias_stride + e];
+          if (A.rbias) l += A.bias_stride == 0 ? bias_e : A.rbias[(size_t)t * A.bias_stride + e];
           A.logits[(size_t)t * A.E + e] = l;
         }
       }
@@ -402,7 +413,7 @@ int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook) {
     pf_split_router<<<256, 256, 0, st>>>(A, L.planes);
     const int nbt = (A.E + 63) / 64, tiles = (A.T + kPfBM - 1) / kPfBM;
     const int nblocks = (tiles * nbt + 7) / 8 * 8;
-    pf_gemm<2><<<nblocks, 256, 0, st>>>(A, L, nbt, nblocks);
+    pf_gemm<2, kPfBM, kPfNS><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   }
@@ -429,7 +440,7 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
     const int nbt = (Imax + kPfBN / 2 - 1) / (kPfBN / 2);
     const int nblocks = (cap * nbt + 7) / 8 * 8;
     hook.pre("pf_gateup", st);
-    pf_gemm<0><<<nblocks, 256, 0, st>>>(A, L, nbt, nblocks);
+    pf_gemm<0, kPfBM, kPfNS><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   }
@@ -437,7 +448,7 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
     const int nbt = (A.H + kPfBN - 1) / kPfBN;
     const int nblocks = (cap * nbt + 7) / 8 * 8;
     hook.pre("pf_down", st);
-    pf_gemm<1><<<nblocks, 256, 0, st>>>(A, L, nbt, nblocks);
+    pf_gemm<1, kPfBM, kPfNS><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   }
