@@ -162,7 +162,10 @@ const char *moe_strerror(int code);
  * synchronises those events, writes for each distinct kernel its name, the
  * number of timed launches and their summed duration in milliseconds
  * (up to max_out entries, *n_out set to the count), destroys the events and
- * turns timing off.  Not thread-safe; for benchmarks only.
+ * turns timing off.  While timing is on, every moe_forward call also times one
+ * empty kernel under the name "launch_overhead": what the event bracketing of
+ * a launch costs with no work, to subtract from the kernels' durations.  Not
+ * thread-safe; for benchmarks only.
  */
 typedef struct {
   char name[64];

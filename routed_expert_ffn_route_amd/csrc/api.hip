@@ -148,6 +148,17 @@ void timing_post(hipStream_t st) {
   ++g_timing.used;
 }
 
+// Empty kernel timed beside the library's own while timing is on: the cost of one event-
+// bracketed launch with no work, which callers subtract from the kernels' durations.
+__global__ void timing_noop() {}
+
+void time_launch_overhead(hipStream_t st) {
+  if (!g_timing.on) return;
+  timing_pre("launch_overhead", st);
+  timing_noop<<<1, 64, 0, st>>>();
+  timing_post(st);
+}
+
 LaunchHook hook() {
   LaunchHook h;
   if (g_timing.on) {
@@ -213,6 +224,7 @@ int moe_forward(const moe_shape_t* shape, const void* x, const moe_weights_t* w,
   if (!aligned16(ws)) return MOE_EALIGN;
   Args A = make_args(shape, x, w, ws);
   A.y = y;
+  time_launch_overhead((hipStream_t)stream);
   if (shape->T <= kDecodeMaxT) return launch_decode(A, (hipStream_t)stream, false, hook());
   return launch_prefill(A, (hipStream_t)stream, hook());
 }
@@ -246,7 +258,9 @@ int moe_timing_begin(int32_t max_launches) {
   g_timing.ev.assign(2 * (size_t)max_launches, nullptr);
   g_timing.names.assign((size_t)max_launches, std::string());
   for (auto& e : g_timing.ev)
-    if (hipEventCreate(&e) != hipSuccess) return MOE_EHIP;
+    // no system-scope fence at each record: timing only, and a fence would add a cache
+    // write-back to every timed launch
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return MOE_EHIP;
   g_timing.used = 0;
   g_timing.on = true;
   return MOE_OK;

@@ -5,6 +5,7 @@ Inputs (CSV from `rocprofv3 --output-format csv`):
   --fetch    a counter_collection.csv from `--pmc FETCH_SIZE --kernel-trace`
   --write    a counter_collection.csv from `--pmc WRITE_SIZE --kernel-trace`
   --kernel   substring of the kernel name to report
+  --label    name the benchmark uses for that kernel (default: --kernel)
   --copy-bytes  size of the plain device-to-device copy the benchmark ran in the counter
              runs (`bench.py --copy-calibration N`): its FETCH_SIZE / WRITE_SIZE per
              dispatch calibrate the counters (factor = N / counter bytes)
@@ -51,11 +52,13 @@ def main():
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
     ap.add_argument("--kernel", required=True)
+    ap.add_argument("--label", default=None)
     ap.add_argument("--copy-bytes", type=int, required=True)
     ap.add_argument("--algorithmic-bytes", type=float, required=True)
     ap.add_argument("--workload", required=True)
     ap.add_argument("--commands", required=True, help="file holding the exact commands run")
     a = ap.parse_args()
+    label = a.label or a.kernel
 
     stats = list(csv.DictReader(open(a.stats)))
     krow = next(r for r in stats if a.kernel in r["Name"])
@@ -71,14 +74,14 @@ def main():
     w_fac = a.copy_bytes / (statistics.median(cw) * 1024)
     traffic = fetch_kib * 1024 * f_fac + write_kib * 1024 * w_fac
     out = {
-        "kernel": a.kernel, "workload": a.workload, "avg_ns": avg_ns,
+        "kernel": label, "kernel_symbol": krow["Name"][:120], "workload": a.workload, "avg_ns": avg_ns,
         "fetch_bytes": round(fetch_kib * 1024 * f_fac), "write_bytes": round(write_kib * 1024 * w_fac),
         "traffic_bytes": round(traffic), "algorithmic_bytes": a.algorithmic_bytes,
         "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
-        "source_hash": source_hash(a.kernel),
+        "source_hash": source_hash(label),
     }
     cmds = open(a.commands).read().strip()
-    print(f"# {a.kernel} -- {a.workload}\n")
+    print(f"# {label} -- {a.workload}\n")
     print("Commands (run from the repository root on one MI355X):\n\n```\n" + cmds + "\n```\n")
     print(f"* mean duration (`--kernel-trace --stats`, {krow['Calls']} calls): {avg_ns / 1e3:.3f} us")
     print(f"* FETCH_SIZE per dispatch: {fetch_kib:.1f} KiB (median of {len(kf)}); "
