@@ -37,5 +37,6 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook);
 // Workspace bytes needed by the prefill path's sections (0 for decode-sized T).
 size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is);
 int prefill_tiles_cap(int T, int E, int k);
+constexpr int kPfTileRows = 128;  // rows per grouped-GEMM tile (the block map's unit)
 
 }  // namespace moe

@@ -28,7 +28,7 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kPfBM = 128;     // rows per tile
+constexpr int kPfBM = kPfTileRows;  // rows per tile
 constexpr int kPfBN = 256;     // B rows per block (gate/up: 128 activation columns x 2)
 constexpr int kPfBK = 32;      // reduction step per LDS stage
 constexpr int kPfNS = 3;       // LDS ring depth (two 256-thread blocks per CU)
@@ -88,11 +88,13 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Blocks are dispatched to the 8 XCDs round-robin; remap so that consecutive logical blocks
-// (same tile / same expert, which share operands) run on the same XCD and share its L2.
-__device__ __forceinline__ int xcd_swizzle(int b, int nblocks) {
-  const int per = nblocks / 8;
-  return (b % 8) * per + b / 8;
+// Blocks are dispatched to the 8 XCDs round-robin; remap the first n blocks so that
+// consecutive logical blocks (same tile / same expert, which share operands) run on the same
+// XCD and share its L2.  A bijection on [0, n) for any n: XCD x takes a contiguous range of
+// n / 8 (+1 for the first n % 8 XCDs) logical blocks.
+__device__ __forceinline__ int xcd_swizzle(int h, int n) {
+  const int x = h % 8, j = h / 8, q = n / 8, r = n % 8;
+  return x * q + min(x, r) + j;
 }
 
 // Router weights -> three bf16 parts per element: hi = w truncated to bf16, mid = the
@@ -186,7 +188,11 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int b = xcd_swizzle(blockIdx.x, nblocks);
+  // the grouped GEMMs' real blocks are the first ntiles * nb_per_tile (the grid is sized for
+  // the worst case); the rest leave at once
+  const int nreal = MODE == 2 ? nblocks : min(nblocks, *L.ntiles * nb_per_tile);
+  if ((int)blockIdx.x >= nreal) return;
+  const int b = xcd_swizzle(blockIdx.x, nreal);
   const int ti = b / nb_per_tile, nb = b - ti * nb_per_tile;
   const int S = A.T * A.k;
   const size_t Imax = A.I > A.Is ? A.I : A.Is;
@@ -195,6 +201,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
   int nrows, pos0 = 0, g = 0, K, N;
   if constexpr (MODE == 2) {
     nrows = min(BM, A.T - ti * BM);
+    if (nrows <= 0) return;
     K = A.H;
     N = A.E;
   } else {
@@ -412,7 +419,7 @@ int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook) {
     hook.pre("pf_router", st);
     pf_split_router<<<256, 256, 0, st>>>(A, L.planes);
     const int nbt = (A.E + 63) / 64, tiles = (A.T + kPfBM - 1) / kPfBM;
-    const int nblocks = (tiles * nbt + 7) / 8 * 8;
+    const int nblocks = tiles * nbt;
     pf_gemm<2, kPfBM, kPfNS><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
@@ -438,7 +445,7 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   const int Imax = A.I > A.Is ? A.I : A.Is;
   {
     const int nbt = (Imax + kPfBN / 2 - 1) / (kPfBN / 2);
-    const int nblocks = (cap * nbt + 7) / 8 * 8;
+    const int nblocks = cap * nbt;
     hook.pre("pf_gateup", st);
     pf_gemm<0, kPfBM, kPfNS><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks);
     hook.post(st);
@@ -446,7 +453,7 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   }
   {
     const int nbt = (A.H + kPfBN - 1) / kPfBN;
-    const int nblocks = (cap * nbt + 7) / 8 * 8;
+    const int nblocks = cap * nbt;
     hook.pre("pf_down", st);
     pf_gemm<1, kPfBM, kPfNS><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks);
     hook.post(st);
