@@ -206,9 +206,10 @@ def main():
     # algorithmic work of one launch of each kernel: bytes for the HBM-bound decode kernels,
     # flops for the prefill GEMMs
     work = {
-        "dec_router_shared": ("hbm", E * H * 4 + 2 * Is * H * ss),
-        "dec_gateup": ("hbm", mean_distinct * gu + Is * H * ss),  # + the shared expert's down rows
-        "dec_down": ("hbm", mean_distinct * dn),
+        "dec_router": ("hbm", E * H * 4),
+        "dec_select": ("hbm", 2 * Is * H * ss),  # the shared expert's gate/up rows (T > 1)
+        "dec_gateup": ("hbm", mean_distinct * gu + (2 * Is * H * ss if T == 1 else 0)),
+        "dec_down": ("hbm", mean_distinct * dn + Is * H * ss),  # + the shared expert's down rows
         "pf_gateup": ("mfma", 2.0 * 2 * (T * k * I + T * Is) * H),
         "pf_down": ("mfma", 2.0 * (T * k * I + T * Is) * H),
         "pf_router": ("mfma", 2.0 * 3 * T * E * H),

@@ -42,7 +42,7 @@ int check_shape(const moe_shape_t* s) {
 }
 
 struct Layout {
-  size_t logits, ids, cw, plan, a_sh, a, y_sh, pf, total;
+  size_t logits, ids, cw, plan, a_sh, a, pf, total;
 };
 
 Layout layout(const moe_shape_t* s) {
@@ -63,8 +63,6 @@ Layout layout(const moe_shape_t* s) {
     off += up(T * (size_t)s->I_shared * 4);
     L.a = off;
     off += up(S * (size_t)s->I * 4);
-    L.y_sh = off;
-    off += up(T * (size_t)s->H * 4);
   } else {
     L.pf = off;
     off += up(prefill_ws_bytes(s->T, s->H, s->E, s->k, s->I, s->I_shared));
@@ -108,7 +106,6 @@ Args make_args(const moe_shape_t* s, const void* x, const moe_weights_t* w, void
     A.plan = (int*)(b + L.plan);
     A.a_sh = (float*)(b + L.a_sh);
     A.a = (float*)(b + L.a);
-    A.y_sh = (float*)(b + L.y_sh);
   } else {
     A.plan = (int*)(b + L.pf);  // prefill sections are carved by the prefill launcher
   }

@@ -40,7 +40,6 @@ struct Args {
   int* plan;            // decode plan, see DecodePlan
   float* a_sh;          // [T][Is]   decode: shared-expert activations (fp32)
   float* a;             // [T*k][I]  decode: routed activations (fp32)
-  float* y_sh;          // [T][H]    decode: shared-expert output (fp32)
   // prefill sections
   int* pf_count;        // [E+1]   (index E = shared expert group)
   int* pf_offset;       // [E+2]
@@ -48,8 +47,6 @@ struct Args {
   int* pf_tiles;        // tile map entries
   uint16_t* pf_act;     // [T*k + T][max(I,Is)] bf16 gate/up activations
   uint16_t* pf_out;     // [T*k + T][H]  bf16 per-row expert outputs (weighted)
-  int router_blocks;    // decode stage-1 grid split
-  int shared_blocks;
   int tiles_cap;        // capacity of pf_tiles
 };
 

@@ -1,21 +1,23 @@
 // Decode path (T <= 16): the layer as four kernels with no cross-block synchronisation
 // inside any of them (a kernel boundary is the cheapest device-wide barrier).
 //
-//  stage 1  router GEMV (fp32 router rows x all T tokens, one wave per expert row) in some
-//           blocks; the shared expert's gate/up GEMV + SwiGLU in the others -- it needs no
-//           routing, so it runs beside the router ("Optimizing on-device inference for Apple
-//           Silicon", section "Overlap independent GPU work").
-//  select   one block: top-k + renormalised softmax per token (one wave each), then the
-//           distinct experts of the window with their tokens, slots and weights (the plan).
-//           A window of several tokens touches up to T*k experts ("Three ways to boost
+//  router   router GEMV: one block per expert row (fp32) x all T tokens.
+//  select   (T > 1) one block: top-k + renormalised softmax per token (one wave each), then
+//           the distinct experts of the window with their tokens, slots and weights (the
+//           plan).  A window of several tokens touches up to T*k experts ("Three ways to boost
 //           mixture-of-experts inference on NVIDIA DGX Spark", section "Optimization 3").
+//           The other blocks of the launch compute the shared expert's gate/up + SwiGLU,
+//           which needs no routing ("Optimizing on-device inference for Apple Silicon",
+//           section "Overlap independent GPU work").
 //  gate/up  block (distinct expert, row tile): streams the expert's gate and up rows once
 //           with 16-byte loads, dots them with every token routed to it and applies SwiGLU
 //           in registers (Apple Silicon page, sections "Optimize the one-row weight path" and
-//           "Reduce intermediate and state traffic").
-//  down     one lane group per output row h: y[t][h] = sum over t's experts of
-//           w * (Wd[e][h] . a) + Wd_s[h] . a_s[t]; the block's waves split the distinct
-//           experts and reduce through LDS in a fixed order, so results are deterministic.
+//           "Reduce intermediate and state traffic").  At T = 1 every block selects the
+//           token's experts itself and the shared gate/up blocks run here instead.
+//  down     one lane group per output row h: y[t][h] = Wd_s[h] . a_s[t] + sum over t's
+//           experts of w * (Wd[e][h] . a); the block's waves split the shared rows' slices and
+//           the distinct experts and reduce through LDS in a fixed order, so results are
+//           deterministic.
 #pragma once
 
 #include <algorithm>
@@ -270,32 +272,47 @@ __device__ __forceinline__ size_t row_bytes(int K) {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
-// Router logits (blocks [0, router_blocks)) and shared-expert gate/up (the rest).
-template <int XT, int SWT, int G, int NCH, int TM, bool XL>
-__global__ __launch_bounds__(kThreads) void dec_stage1(Args A) {
-  extern __shared__ uint4 s_x1[];
+// Router logits: block e computes logits[t][e] = Wr[e] . x[t] (+ bias) for every token.  Its
+// four waves take contiguous quarters of H (up to four 16-byte chunks per lane in flight per
+// pass) and meet in LDS, where wave 0 adds the four partial sums in a fixed order.  One block
+// per expert spreads the fp32 router rows over the whole chip.
+constexpr int kRouterChunks = 4;
+template <int XT, int TM>
+__global__ __launch_bounds__(kThreads) void dec_router(Args A) {
+  __shared__ float s_p[kWaves][TM];
   const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  if ((int)blockIdx.x < A.router_blocks) {
-    const int e = blockIdx.x * kWaves + wave;
-    if (e >= A.E) return;
-    if (A.logits_in) {  // moe_route on given logits: copy, no router
-      for (int t = lane; t < A.T; t += kWave) {
-        const float l = A.logits_in[(size_t)t * A.E + e];
-        A.logits[(size_t)t * A.E + e] = l;
-        if (A.o_logits) A.o_logits[(size_t)t * A.E + e] = l;
-      }
-      return;
+  const int e = blockIdx.x;
+  if (A.logits_in) {  // routing on given logits: copy them, no router
+    for (int t = threadIdx.x; t < A.T; t += blockDim.x) {
+      const float l = A.logits_in[(size_t)t * A.E + e];
+      A.logits[(size_t)t * A.E + e] = l;
+      if (A.o_logits) A.o_logits[(size_t)t * A.E + e] = l;
     }
-    const float* wr = A.rw + (size_t)e * A.H;
-    const uint8_t* xb = (const uint8_t*)A.x;
-    const size_t xstride = (size_t)A.H * XS<XT>::BYTES;
-    float acc[TM];
+    return;
+  }
+  const float* wr = A.rw + (size_t)e * A.H;
+  const uint8_t* xb = (const uint8_t*)A.x;
+  const size_t xstride = (size_t)A.H * XS<XT>::BYTES;
+  const int nch = A.H / 4;  // float4 chunks of the row
+  const int per = (nch + kWaves - 1) / kWaves;
+  const int cb = wave * per, ce = min(nch, cb + per);
+  float acc[TM];
 #pragma unroll
-    for (int t = 0; t < TM; ++t) acc[t] = 0.f;
-    const int nch = A.H / 4;
-#pragma unroll 8
-    for (int c = lane; c < nch; c += kWave) {
-      const float4 w = ldf4(wr + (size_t)c * 4);
+  for (int t = 0; t < TM; ++t) acc[t] = 0.f;
+  for (int c0 = cb; c0 < ce; c0 += kWave * kRouterChunks) {
+    float4 w[kRouterChunks];
+    int cc[kRouterChunks];
+    float okf[kRouterChunks];  // chunks past the quarter's end load chunk 0 and count 0 times
+#pragma unroll
+    for (int m = 0; m < kRouterChunks; ++m) {
+      const int c = c0 + lane + kWave * m;
+      const bool ok = c < ce;
+      cc[m] = ok ? c : 0;
+      okf[m] = ok ? 1.f : 0.f;
+      w[m] = ldf4(wr + (size_t)cc[m] * 4);
+    }
+#pragma unroll
+    for (int m = 0; m < kRouterChunks; ++m) {
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
         // no branch around the x loads, so that they issue together with the weight loads;
@@ -303,61 +320,85 @@ __global__ __launch_bounds__(kThreads) void dec_stage1(Args A) {
         const int tt = t < A.T ? t : 0;
         float x0, x1, x2, x3;
         if constexpr (XT == MOE_F32) {
-          const float4 xv = *(const float4*)(xb + tt * xstride + (size_t)c * 16);
+          const float4 xv = *(const float4*)(xb + tt * xstride + (size_t)cc[m] * 16);
           x0 = xv.x; x1 = xv.y; x2 = xv.z; x3 = xv.w;
         } else {
-          const uint2 xv = ldg8(xb + tt * xstride + (size_t)c * 8);
+          const uint2 xv = ldg8(xb + tt * xstride + (size_t)cc[m] * 8);
           x0 = bf16lo(xv.x); x1 = bf16hi(xv.x); x2 = bf16lo(xv.y); x3 = bf16hi(xv.y);
         }
-        acc[t] = fmaf(w.x, x0, acc[t]);
-        acc[t] = fmaf(w.y, x1, acc[t]);
-        acc[t] = fmaf(w.z, x2, acc[t]);
-        acc[t] = fmaf(w.w, x3, acc[t]);
+        float d = w[m].x * x0;
+        d = fmaf(w[m].y, x1, d);
+        d = fmaf(w[m].z, x2, d);
+        d = fmaf(w[m].w, x3, d);
+        acc[t] = fmaf(okf[m], d, acc[t]);
       }
     }
+  }
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      if (t < A.T) {
-        float s = group_sum<kWave>(acc[t]);
-        if (lane == 0) {
-          if (A.rbias) s += A.rbias[(size_t)t * A.bias_stride + e];
-          A.logits[(size_t)t * A.E + e] = s;
-          if (A.o_logits) A.o_logits[(size_t)t * A.E + e] = s;
-        }
-      }
-    }
-  } else {
-    constexpr int RB = kWave / G;
-    const int grp = lane / G, gl = lane % G;
-    const int row = (blockIdx.x - A.router_blocks) * (kWaves * RB) + wave * RB + grp;
-    const bool valid = row < A.Is;
-    const int r = valid ? row : 0;
-    const size_t rb = row_bytes<SWT>(A.H);
-    int slots[TM];
+  for (int t = 0; t < TM; ++t) {
+    const float v = group_sum<kWave>(acc[t]);
+    if (lane == 0) s_p[wave][t] = v;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < A.T) {
+    float s = s_p[0][t];
 #pragma unroll
-    for (int t = 0; t < TM; ++t) slots[t] = t;
-    const unsigned mask = (A.T >= 32) ? 0xffffffffu : ((1u << A.T) - 1u);
-    const size_t xstride = (size_t)A.H * XS<XT>::BYTES;
-    gateup_row<XT, SWT, G, NCH, TM, XL>((const uint8_t*)A.sgate + r * rb,
-                                        (const uint8_t*)A.sup + r * rb, nullptr, nullptr,
-                                        A.H / GU<SWT>::EPC, (const uint8_t*)A.x, s_x1,
-                                        (int)(A.T * xstride), xstride, mask, slots, A.a_sh, A.Is,
-                                        row, gl, valid);
+    for (int w = 1; w < kWaves; ++w) s += s_p[w][t];
+    if (A.rbias) s += A.rbias[(size_t)t * A.bias_stride + e];
+    A.logits[(size_t)t * A.E + e] = s;
+    if (A.o_logits) A.o_logits[(size_t)t * A.E + e] = s;
   }
 }
 
-// Selection and the decode plan: one block, wave t selects token t (select_set: the k
-// largest logits, ties to the lower index, renormalised softmax weights), then the distinct
-// experts are compacted in ascending id with one ballot per 64 experts.
-__global__ __launch_bounds__(kWave * kDecodeMaxT) void dec_select(Args A) {
-  __shared__ int s_ids[kDecodeMaxT * MOE_MAX_K];
-  __shared__ float s_w[kDecodeMaxT * MOE_MAX_K];
+// The shared expert's gate/up + SwiGLU for every token: one wave per shared row (the 64 lanes
+// split K = H, kShNch chunks each per pass), a_sh[t][row] = silu(g) * u.  It needs no routing,
+// so it runs in the blocks of a kernel that would otherwise leave HBM idle while it selects
+// ("Optimizing on-device inference for Apple Silicon", section "Overlap independent GPU
+// work").  Every thread of the block must call it (XL stages x in LDS behind a barrier).
+constexpr int kShNch = 5;
+template <int XT, int SWT, int TM, bool XL>
+__device__ __forceinline__ void shared_gateup_block(const Args& A, int blk, int lane, int wave,
+                                                    uint4* s_x) {
+  const int nw = blockDim.x / kWave;
+  const int row = blk * nw + wave;
+  const bool valid = row < A.Is;
+  const size_t r = valid ? row : 0;
+  const size_t rb = row_bytes<SWT>(A.H);
+  int slots[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) slots[t] = t;
+  const unsigned mask = (A.T >= 32) ? 0xffffffffu : ((1u << A.T) - 1u);
+  const size_t xstride = (size_t)A.H * XS<XT>::BYTES;
+  gateup_row<XT, SWT, kWave, kShNch, TM, XL>((const uint8_t*)A.sgate + r * rb,
+                                             (const uint8_t*)A.sup + r * rb, nullptr, nullptr,
+                                             A.H / GU<SWT>::EPC, (const uint8_t*)A.x, s_x,
+                                             (int)(A.T * xstride), xstride, mask, slots, A.a_sh,
+                                             A.Is, row, lane, valid);
+}
+
+// Selection and the decode plan (T > 1): the last block; wave t selects token t (select_set:
+// the k largest logits, ties to the lower index, renormalised softmax weights), then the
+// distinct experts are compacted in ascending id with one ballot per 64 experts.  The
+// blocks before it compute the shared expert's gate/up (shared_gateup_block), which keeps HBM
+// busy while the selection runs.  Block size 64 * TM (TM >= T).
+template <int XT, int SWT, int TM, bool XL>
+__global__ __launch_bounds__(kWave * TM) void dec_select(Args A, int nsh) {
+  extern __shared__ uint4 s_xs[];
+  const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if ((int)blockIdx.x < nsh) {
+    shared_gateup_block<XT, SWT, TM, XL>(A, blockIdx.x, lane, wave, s_xs);
+    return;
+  }
+  __shared__ int s_ids[TM * MOE_MAX_K];
+  __shared__ float s_w[TM * MOE_MAX_K];
   __shared__ unsigned s_flag[MOE_MAX_E];
   __shared__ int s_pos[MOE_MAX_E];
-  __shared__ int s_dslot[kDecodeMaxT * MOE_MAX_K * kDecodeMaxT];
-  __shared__ float s_dw[kDecodeMaxT * MOE_MAX_K * kDecodeMaxT];
+  __shared__ int s_dslot[TM * MOE_MAX_K * TM];
+  __shared__ float s_dw[TM * MOE_MAX_K * TM];
+  __shared__ unsigned s_hist[TM][512];
   __shared__ int s_nd;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave, nth = blockDim.x;
+  const int nth = blockDim.x;
   const int T = A.T, k = A.k, E = A.E, S = T * k, D = S < E ? S : E;
   const DecodePlan P(A.plan, D, T);
   for (int i = threadIdx.x; i < E; i += nth) s_flag[i] = 0u;
@@ -365,7 +406,6 @@ __global__ __launch_bounds__(kWave * kDecodeMaxT) void dec_select(Args A) {
     s_dslot[i] = 0;
     s_dw[i] = 0.f;
   }
-  __shared__ unsigned s_hist[kDecodeMaxT][512];
   if (wave < T)
     select_set(A.logits + (size_t)wave * E, E, k, lane, s_hist[wave], s_ids + wave * k, s_w + wave * k);
   __syncthreads();
@@ -412,11 +452,10 @@ __global__ __launch_bounds__(kWave * kDecodeMaxT) void dec_select(Args A) {
 // before step p is consumed, and no buffer is ever copied into the other (a register copy
 // would wait for the copied loads).  At the end the last step is loaded once more (cache-
 // resident) instead of branching around the load, which keeps the wait counts exact.
+// stream_loaded: buffer a already holds step 0.
 template <class Buf, class Load, class Consume>
-__device__ __forceinline__ void stream_steps(int np, Load load, Consume consume) {
+__device__ __forceinline__ void stream_loaded(int np, Buf& a, Buf& b, Load load, Consume consume) {
   if (np <= 0) return;  // uniform
-  Buf a, b;
-  load(0, a);
   for (int p = 0;; p += 2) {
     const bool more1 = p + 1 < np;
     load(more1 ? p + 1 : p, b);
@@ -429,60 +468,18 @@ __device__ __forceinline__ void stream_steps(int np, Load load, Consume consume)
   }
 }
 
-// Shared expert's down projection, y_sh[t][h] = Wd_s[h] . a_s[t] (fp32), for 16 rows per
-// block (four per wave, 16 lanes per row).  It depends only on the stage-1 activations, so it
-// runs inside the gate/up kernel beside the routed rows, and the down kernel only adds it.
-constexpr int kShRowsPerBlock = kWaves * 4;
-template <int SWT, int TM>
-__device__ __forceinline__ void shared_down_rows(const Args& A, int blk, int lane, int wave) {
-  constexpr int G = 16, NCH = 2;
-  const int grp = lane / G, gl = lane % G;
-  const int h = blk * kShRowsPerBlock + wave * (kWave / G) + grp;
-  const bool valid = h < A.H;
-  const int nchs = A.Is / DN<SWT>::EPC;
-  const uint8_t* srow = (const uint8_t*)A.sdown + (size_t)(valid ? h : 0) * row_bytes<SWT>(A.Is);
-  float acc[TM];
-#pragma unroll
-  for (int t = 0; t < TM; ++t) acc[t] = 0.f;
-  for (int c0 = 0; c0 < nchs; c0 += G * NCH) {
-    typename DN<SWT>::W w[NCH];
-    int cc[NCH];
-    float okf[NCH];
-#pragma unroll
-    for (int m = 0; m < NCH; ++m) {
-      const int c = c0 + gl + G * m;
-      cc[m] = c < nchs ? c : 0;
-      okf[m] = c < nchs ? 1.f : 0.f;
-      w[m] = DN<SWT>::load(srow, cc[m]);
-    }
-#pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      if (t >= A.T) break;  // uniform
-#pragma unroll
-      for (int m = 0; m < NCH; ++m)
-        acc[t] = fmaf(okf[m], DN<SWT>::dot(w[m], A.a_sh + (size_t)t * A.Is, cc[m]), acc[t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < TM; ++t) {
-    const float v = group_sum<G>(acc[t]);
-    if (gl == 0 && valid && t < A.T) A.y_sh[(size_t)t * A.H + h] = v;
-  }
-}
-
 // Gate/up + SwiGLU: block (u, tile) streams RB rows per wave of distinct expert u's gate and
-// up matrices once and dots them with every token routed to u.  The first sh_blocks blocks
-// compute the shared expert's down projection instead.  XL: x is staged in LDS
+// up matrices once and dots them with every token routed to u.  XL: x is staged in LDS
 // (dynamic shared memory of T * H * sizeof(x) bytes).  SEL1 (T = 1, no selection kernel):
 // wave 0 of every block selects the token's experts from the logits itself -- the k experts
 // are then the distinct experts, in ascending id -- and block 0 publishes the plan for the
-// down kernel.
+// down kernel; the first sh_blocks blocks compute the shared expert's gate/up meanwhile.
 template <int XT, int WT, int SWT, int G, int NCH, int TM, bool XL, bool SEL1>
 __global__ __launch_bounds__(kThreads) void dec_gateup(Args A, int tiles, int sh_blocks) {
   extern __shared__ uint4 s_x[];
   const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if ((int)blockIdx.x < sh_blocks) {
-    shared_down_rows<SWT, TM>(A, blockIdx.x, lane, wave);
+    shared_gateup_block<XT, SWT, TM, XL>(A, blockIdx.x, lane, wave, s_x);
     return;
   }
   const int blk = blockIdx.x - sh_blocks;
@@ -535,22 +532,23 @@ __global__ __launch_bounds__(kThreads) void dec_gateup(Args A, int tiles, int sh
                                      valid);
 }
 
-// Down + combine: y[t][h] = sum over t's experts of w * (Wd[e][h] . a) + y_sh[t][h].
+// Down + combine: y[t][h] = Wd_s[h] . a_s[t] + sum over t's experts of w * (Wd[e][h] . a).
 // Output rows come in groups of RB (one lane group of G lanes per row); a block takes row
-// groups blockIdx.x, blockIdx.x + gridDim.x, ... and its NW waves share the work items
-// (row group, K-slice, distinct expert) round robin.  The plan and -- when it fits (ALDS) --
-// every routed activation row are staged in LDS once per block; each wave then streams its
-// items' 16-byte weight chunks with the next item's loads in flight while it consumes the
-// current one.  Per (row group, wave) partial sums go to LDS and are added in a fixed order
-// at the end, so the result is deterministic.
+// groups blockIdx.x, blockIdx.x + gridDim.x, ... and its NW waves share the work items round
+// robin: first (row group, K-slice) of the shared expert, then (row group, K-slice, distinct
+// expert) of the routed ones.  The plan and -- when they fit (ALDS) -- every routed and shared
+// activation row are staged in LDS once per block; a wave whose first item is a shared one
+// has that item's weights in flight before the staging barrier (they need no plan).  Each wave
+// streams its items' 16-byte weight chunks with the next item's loads in flight while it
+// consumes the current one.  Per (row group, wave) partial sums are added up in LDS and summed
+// over the waves in a fixed order at the end, so the result is deterministic.
 // Dynamic LDS (4-byte words): plan (2D + 2DT), partials [nrgb_max][NW][TM][RB], then ALDS
-// activations [T*k][I].
-template <int WT, int G, int NCH, int TM, bool ALDS>
-__global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, int act_off) {
+// activations [T*k][I] at act_off and [T][Is] at ash_off.
+template <int WT, int SWT, int G, int NCH, int TM, bool ALDS>
+__global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, int act_off, int ash_off) {
   extern __shared__ float s_f[];
-  typedef typename DN<WT>::W W;
+  static_assert(sizeof(typename DN<WT>::W) == 16 && sizeof(typename DN<SWT>::W) == 16, "16-byte chunks");
   constexpr int RB = kWave / G;
-  constexpr int EPC = DN<WT>::EPC;
   const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int NW = blockDim.x / kWave;
   const int grp = lane / G, gl = lane % G;
@@ -562,7 +560,123 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
   float* s_w = s_f + 2 * D + D * T;
   float* s_part = s_f + 2 * D + 2 * D * T;
   float* s_act = s_f + act_off;
-  const int nd = *P.nd();
+  float* s_ash = s_f + ash_off;
+
+  const int nch = A.I / DN<WT>::EPC;
+  const int nsl = (nch + G * NCH - 1) / (G * NCH);
+  const int nchs = A.Is / DN<SWT>::EPC;
+  const int nsls = (nchs + G * NCH - 1) / (G * NCH);
+  const int nrgb = (nrg - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
+  const int nqs = nrgb * nsls;  // shared items
+  const size_t rb = row_bytes<WT>(A.I), rbs = row_bytes<SWT>(A.Is);
+  const float* abase = ALDS ? s_act : A.a;
+  const float* asbase = ALDS ? s_ash : A.a_sh;
+
+  float acc[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) acc[t] = 0.f;
+  int cur_j = -1;
+  int nd = 0, per_rg = 0;  // routed items per row group, known once the plan is read
+  struct Buf {
+    uint4 w[NCH];
+    uint32_t sb[NCH];
+  };
+  auto row_of = [&](int j) { return ((int)blockIdx.x + j * (int)gridDim.x) * RB + grp; };
+  auto load = [&](int q, Buf& bf) {
+    if (q < nqs) {  // uniform: shared item (row group j, slice sl)
+      const int j = q / nsls, sl = q - j * nsls;
+      const int h = row_of(j), hh = h < A.H ? h : 0;
+      const uint8_t* row = (const uint8_t*)A.sdown + (size_t)hh * rbs;
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) {
+        const int c = sl * G * NCH + gl + G * m;
+        bf.w[m] = DN<SWT>::load(row, c < nchs ? c : 0);
+      }
+      return;
+    }
+    const int r = q - nqs;
+    const int j = r / per_rg, r2 = r - j * per_rg;
+    const int sl = r2 / nd, u = r2 - sl * nd;
+    const int h = row_of(j), hh = h < A.H ? h : 0;
+    const int e = s_e[u];
+    const uint8_t* row = (const uint8_t*)A.down + ((size_t)e * A.H + hh) * rb;
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const int c = sl * G * NCH + gl + G * m;
+      const int cc = c < nch ? c : 0;
+      bf.w[m] = DN<WT>::load(row, cc);
+      if constexpr (WT == MOE_MXFP4) bf.sb[m] = A.ds[((size_t)e * A.H + hh) * (A.I / 32) + cc];
+    }
+  };
+  auto flush = [&]() {
+    if (cur_j < 0) return;  // uniform
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const float v = group_sum<G>(acc[t]);
+      // a wave meets a row group at most twice (shared, then routed items): accumulate
+      if (gl == 0) s_part[((cur_j * NW + wave) * TM + t) * RB + grp] += v;
+      acc[t] = 0.f;
+    }
+  };
+  // one body for both kinds of item (two copies of the token loop would double the live
+  // registers): a shared item is every token with weight 1 over a_sh's rows
+  const unsigned all_t = (T >= 32) ? 0xffffffffu : ((1u << T) - 1u);
+  auto consume = [&](int q, const Buf& bf) {
+    const bool sh = q < nqs;  // uniform
+    int j, sl, u = 0;
+    if (sh) {
+      j = q / nsls;
+      sl = q - j * nsls;
+    } else {
+      const int r = q - nqs;
+      j = r / per_rg;
+      const int r2 = r - j * per_rg;
+      sl = r2 / nd;
+      u = r2 - sl * nd;
+    }
+    if (j != cur_j) {  // uniform
+      flush();
+      cur_j = j;
+    }
+    const int lim = sh ? nchs : nch;
+    int cc[NCH];
+    float sc[NCH];
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const int c = sl * G * NCH + gl + G * m;
+      cc[m] = c < lim ? c : 0;
+      if constexpr (WT == MOE_MXFP4)  // select, not multiply: a NaN scale must not leak
+        sc[m] = c < lim ? (sh ? 1.f : e8m0_to_f32(bf.sb[m])) : 0.f;
+      else
+        sc[m] = c < lim ? 1.f : 0.f;
+    }
+    const unsigned mask = sh ? all_t : s_m[u];
+    const float* ab = sh ? asbase : abase;
+    const int ld = sh ? A.Is : A.I;
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (!((mask >> t) & 1u)) continue;  // uniform
+      const float* arow = ab + (size_t)(sh ? t : s_sl[u * T + t]) * ld;
+      const float wt = sh ? 1.f : s_w[u * T + t];
+      float part = 0.f;
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) {
+        float d;
+        if constexpr (WT == SWT)
+          d = DN<WT>::dot(bf.w[m], arow, cc[m]);
+        else
+          d = sh ? DN<SWT>::dot(bf.w[m], arow, cc[m]) : DN<WT>::dot(bf.w[m], arow, cc[m]);
+        part = fmaf(sc[m], d, part);
+      }
+      acc[t] = fmaf(wt, part, acc[t]);
+    }
+  };
+
+  // this wave's items are q = wave + NW * step; a shared first item needs no plan
+  Buf a, b;
+  const bool pre = wave < nqs;  // uniform
+  if (pre) load(wave, a);
+  nd = *P.nd();
   for (int i = threadIdx.x; i < D; i += blockDim.x) {
     s_e[i] = P.dexp()[i];
     s_m[i] = P.dmask()[i];
@@ -575,94 +689,19 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
   if constexpr (ALDS) {
     const int n4 = S * A.I / 4;
     for (int i = threadIdx.x; i < n4; i += blockDim.x) ((float4*)s_act)[i] = ldf4(A.a + (size_t)i * 4);
+    const int n4s = T * A.Is / 4;
+    for (int i = threadIdx.x; i < n4s; i += blockDim.x) ((float4*)s_ash)[i] = ldf4(A.a_sh + (size_t)i * 4);
   }
   __syncthreads();
-
-  const int nch = A.I / EPC;
-  const int nsl = (nch + G * NCH - 1) / (G * NCH);
-  const int per_rg = nsl * nd;
-  const int nrgb = (nrg - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
-  const int nq = nrgb * per_rg;
-  const size_t rb = row_bytes<WT>(A.I);
-  const float* abase = ALDS ? s_act : A.a;
-
-  float acc[TM];
-#pragma unroll
-  for (int t = 0; t < TM; ++t) acc[t] = 0.f;
-  int cur_j = -1;
-  // item q -> (row group j of this block, slice sl, distinct expert u)
-  auto item = [&](int q, int& j, int& sl, int& u) {
-    j = q / per_rg;
-    const int r = q - j * per_rg;
-    sl = r / nd;
-    u = r - sl * nd;
-  };
-  struct Buf {
-    W w[NCH];
-    uint32_t sb[NCH];
-  };
-  auto load = [&](int q, Buf& bf) {
-    W* w = bf.w;
-    uint32_t* sb = bf.sb;
-    int j, sl, u;
-    item(q, j, sl, u);
-    const int h = ((int)blockIdx.x + j * (int)gridDim.x) * RB + grp;
-    const int hh = h < A.H ? h : 0;
-    const int e = s_e[u];
-    const uint8_t* row = (const uint8_t*)A.down + ((size_t)e * A.H + hh) * rb;
-#pragma unroll
-    for (int m = 0; m < NCH; ++m) {
-      const int c = sl * G * NCH + gl + G * m;
-      const int cc = c < nch ? c : 0;
-      w[m] = DN<WT>::load(row, cc);
-      if constexpr (WT == MOE_MXFP4) sb[m] = A.ds[((size_t)e * A.H + hh) * (A.I / 32) + cc];
-    }
-  };
-  auto flush = [&]() {
-    if (cur_j < 0) return;  // uniform
-#pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      const float v = group_sum<G>(acc[t]);
-      if (gl == 0) s_part[((cur_j * NW + wave) * TM + t) * RB + grp] = v;
-      acc[t] = 0.f;
-    }
-  };
-  auto consume = [&](int q, const Buf& bf) {
-    const W* w = bf.w;
-    const uint32_t* sb = bf.sb;
-    int j, sl, u;
-    item(q, j, sl, u);
-    if (j != cur_j) {  // uniform
-      flush();
-      cur_j = j;
-    }
-    int cc[NCH];
-    float sc[NCH];
-#pragma unroll
-    for (int m = 0; m < NCH; ++m) {
-      const int c = sl * G * NCH + gl + G * m;
-      cc[m] = c < nch ? c : 0;
-      if constexpr (WT == MOE_MXFP4)  // select, not multiply: a NaN scale must not leak
-        sc[m] = c < nch ? e8m0_to_f32(sb[m]) : 0.f;
-      else
-        sc[m] = c < nch ? 1.f : 0.f;
-    }
-    const unsigned mask = s_m[u];
-#pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      if (!((mask >> t) & 1u)) continue;  // uniform
-      const float* arow = abase + (size_t)s_sl[u * T + t] * A.I;
-      float part = 0.f;
-#pragma unroll
-      for (int m = 0; m < NCH; ++m) part = fmaf(sc[m], DN<WT>::dot(w[m], arow, cc[m]), part);
-      acc[t] = fmaf(s_w[u * T + t], part, acc[t]);
-    }
-  };
-  // this wave's items are q = wave + NW * step
+  per_rg = nsl * nd;
+  const int nq = nqs + nrgb * per_rg;
   const int nmine = wave < nq ? (nq - 1 - wave) / NW + 1 : 0;
-  stream_steps<Buf>(nmine, [&](int st, Buf& bf) { load(wave + NW * st, bf); },
-                    [&](int st, const Buf& bf) { consume(wave + NW * st, bf); });
-  if (nmine > 0) flush();
+  if (nmine > 0) {  // uniform
+    if (!pre) load(wave, a);
+    stream_loaded<Buf>(nmine, a, b, [&](int st, Buf& bf) { load(wave + NW * st, bf); },
+                       [&](int st, const Buf& bf) { consume(wave + NW * st, bf); });
+    flush();
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < nrgb * TM * RB; i += blockDim.x) {
     const int j = i / (TM * RB), r = i - j * (TM * RB);
@@ -671,7 +710,6 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
     if (t < T && h < A.H) {
       float v = 0.f;
       for (int w = 0; w < NW; ++w) v += s_part[((j * NW + w) * TM + t) * RB + g];
-      if (A.Is > 0) v += A.y_sh[(size_t)t * A.H + h];
       if (A.odt == MOE_BF16)
         ((uint16_t*)A.y)[(size_t)t * A.H + h] = f32_to_bf16(v);
       else
@@ -750,30 +788,6 @@ int pick_down(int nchunks, int H, int ncu) {
   return best >= 0 ? best : pick_gn(kDN, nchunks);
 }
 
-// Resident blocks per CU of kernel f at this block size and dynamic LDS (cached).
-int blocks_per_cu(const void* f, int threads, size_t lds) {
-  struct E { const void* f; int threads; size_t lds; int n; };
-  static E cache[256];
-  static int used = 0;
-  static std::mutex mu;
-  std::lock_guard<std::mutex> lock(mu);
-  for (int i = 0; i < used; ++i)
-    if (cache[i].f == f && cache[i].threads == threads && cache[i].lds == lds) return cache[i].n;
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, threads, lds) != hipSuccess || n < 1) n = 1;
-  if (used < 256) cache[used++] = E{f, threads, lds, n};
-  return n;
-}
-
-template <int XT, int SWT, int TM, const GN* L, bool XL>
-void* stage1_fn(int gi) {
-  switch (gi) {
-#define C(i) case i: return (void*)dec_stage1<XT, SWT, L[i].G, L[i].NCH, TM, XL>;
-    C(0) C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8) C(9)
-#undef C
-  }
-  return nullptr;
-}
 template <int XT, int WT, int SWT, int TM, const GN* L, bool XL, bool SEL1>
 void* gateup_fn(int gi) {
   switch (gi) {
@@ -783,10 +797,10 @@ void* gateup_fn(int gi) {
   }
   return nullptr;
 }
-template <int WT, int TM, bool ALDS>
+template <int WT, int SWT, int TM, bool ALDS>
 void* down_fn(int gi) {
   switch (gi) {
-#define C(i) case i: return (void*)dec_down<WT, kDN[i].G, kDN[i].NCH, TM, ALDS>;
+#define C(i) case i: return (void*)dec_down<WT, SWT, kDN[i].G, kDN[i].NCH, TM, ALDS>;
     C(0) C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8) C(9) C(10) C(11)
 #undef C
   }
@@ -795,48 +809,53 @@ void* down_fn(int gi) {
 
 int gu_epc(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : 32; }
 int dn_epc(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : 32; }
-constexpr int kMaxLdsX = 64 * 1024;  // x staged in LDS by the gate/up kernel up to this size
+constexpr int kMaxLdsX = 64 * 1024;  // x staged in LDS by the gate/up kernels up to this size
+
+hipError_t launch_dyn(const void* f, dim3 grid, dim3 block, void** args, size_t lds, hipStream_t st) {
+  if (lds > 65536 && hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return hipErrorInvalidValue;
+  return hipLaunchKernel(f, grid, block, args, lds, st);
+}
 
 template <int XT, int WT, int SWT, int TM>
 int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& hook) {
   constexpr const GN* GUL = TM == 1 ? kGU1 : kGUn;
   const DevInfo dv = dev_info();
   const int S = A.T * A.k, D = S < A.E ? S : A.E;
-  const int g1 = pick_gn(TM == 1 ? kGU1 : kGUn, A.H / gu_epc(SWT));
-  const int rb1 = kWaves * (kWave / GUL[g1].G);
-  A.router_blocks = (A.E + kWaves - 1) / kWaves;
-  A.shared_blocks = (route_only || A.Is == 0) ? 0 : (A.Is + rb1 - 1) / rb1;
-  // x goes through LDS where several tokens meet each weight chunk
-  const size_t xbytes = (size_t)A.T * A.H * (XT == MOE_F32 ? 4 : 2);
-  const bool xl = TM > 1 && xbytes <= kMaxLdsX;
-  void* f1 = xl ? stage1_fn<XT, SWT, TM, GUL, true>(g1) : stage1_fn<XT, SWT, TM, GUL, false>(g1);
-
   void* args1[] = {&A};
-  hook.pre("dec_router_shared", st);
-  hipError_t err = hipLaunchKernel(f1, dim3(A.router_blocks + A.shared_blocks), dim3(kThreads), args1,
-                                   xl ? xbytes : 0, st);
+  hook.pre("dec_router", st);
+  hipError_t err = hipLaunchKernel((void*)dec_router<XT, TM>, dim3(A.E), dim3(kThreads), args1, 0, st);
   hook.post(st);
   if (err != hipSuccess) return MOE_EHIP;
   if (route_only) return MOE_OK;
 
-  if (TM > 1) {  // T = 1 selects inside the gate/up kernel
+  // x goes through LDS where several tokens meet each weight chunk
+  const size_t xbytes = (size_t)A.T * A.H * (XT == MOE_F32 ? 4 : 2);
+  const bool xl = TM > 1 && xbytes <= kMaxLdsX;
+  // shared expert gate/up: one row per wave, in the selection kernel (T > 1) or beside the
+  // routed rows of the gate/up kernel (T = 1)
+  const int sh_waves = TM == 1 ? kWaves : TM;
+  int nsh = A.Is > 0 ? (A.Is + sh_waves - 1) / sh_waves : 0;
+  if (TM > 1) {
+    void* fs = xl ? (void*)dec_select<XT, SWT, TM, true> : (void*)dec_select<XT, SWT, TM, false>;
+    void* args_s[] = {&A, &nsh};
     hook.pre("dec_select", st);
-    err = hipLaunchKernel((void*)dec_select, dim3(1), dim3(kWave * A.T), args1, 0, st);
+    err = launch_dyn(fs, dim3(nsh + 1), dim3(kWave * TM), args_s, xl ? xbytes : 0, st);
     hook.post(st);
     if (err != hipSuccess) return MOE_EHIP;
   }
 
-  // gate/up: shared-expert down blocks first, then (distinct expert, row tile) blocks
-  const int g2 = pick_gn(TM == 1 ? kGU1 : kGUn, A.H / gu_epc(WT));
+  // gate/up: (T = 1: shared gate/up blocks first, then) (distinct expert, row tile) blocks
+  const int g2 = TM == 1 ? pick_gn(kGU1, A.H / gu_epc(WT)) : pick_gn(kGUn, A.H / gu_epc(WT));
   const int rb2 = kWaves * (kWave / GUL[g2].G);
   int tiles = (A.I + rb2 - 1) / rb2;
-  int sh_blocks = A.Is > 0 ? (A.H + kShRowsPerBlock - 1) / kShRowsPerBlock : 0;
+  int sh_blocks = TM == 1 ? nsh : 0;
   void* f2 = TM == 1 ? gateup_fn<XT, WT, SWT, TM, GUL, false, true>(g2)
              : xl    ? gateup_fn<XT, WT, SWT, TM, GUL, true, false>(g2)
                      : gateup_fn<XT, WT, SWT, TM, GUL, false, false>(g2);
   void* args2[] = {&A, &tiles, &sh_blocks};
   hook.pre("dec_gateup", st);
-  err = hipLaunchKernel(f2, dim3(sh_blocks + D * tiles), dim3(kThreads), args2, xl ? xbytes : 0, st);
+  err = launch_dyn(f2, dim3(sh_blocks + D * tiles), dim3(kThreads), args2, xl ? xbytes : 0, st);
   hook.post(st);
   if (err != hipSuccess) return MOE_EHIP;
 
@@ -849,15 +868,14 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   constexpr int nw = 16;
   const size_t plan_w = 2 * (size_t)D + 2 * (size_t)D * A.T;
   int act_off = (int)((plan_w + (size_t)nrgb * nw * TM * rb3 + 3) / 4 * 4);
-  const size_t lds_act = (size_t)act_off * 4 + (size_t)S * A.I * 4;
+  int ash_off = (int)(act_off + ((size_t)S * A.I + 3) / 4 * 4);
+  const size_t lds_act = (size_t)ash_off * 4 + (size_t)A.T * A.Is * 4;
   const bool alds = lds_act <= (size_t)dv.max_lds;
   const size_t lds3 = alds ? lds_act : (size_t)act_off * 4;
-  void* f3 = alds ? down_fn<WT, TM, true>(g3) : down_fn<WT, TM, false>(g3);
-  if (lds3 > 65536 && hipFuncSetAttribute(f3, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3) != hipSuccess)
-    return MOE_EHIP;
-  void* args3[] = {&A, &nrg, &nrgb, &act_off};
+  void* f3 = alds ? down_fn<WT, SWT, TM, true>(g3) : down_fn<WT, SWT, TM, false>(g3);
+  void* args3[] = {&A, &nrg, &nrgb, &act_off, &ash_off};
   hook.pre("dec_down", st);
-  err = hipLaunchKernel(f3, dim3(grid3), dim3(kWave * nw), args3, lds3, st);
+  err = launch_dyn(f3, dim3(grid3), dim3(kWave * nw), args3, lds3, st);
   hook.post(st);
   if (err != hipSuccess) return MOE_EHIP;
   return MOE_OK;
@@ -867,6 +885,7 @@ template <int XT, int WT, int SWT>
 int launch_decode_dt(Args A, hipStream_t st, bool route_only, const LaunchHook& hook) {
   if (A.T <= 1) return launch_decode_t<XT, WT, SWT, 1>(A, st, route_only, hook);
   if (A.T <= 4) return launch_decode_t<XT, WT, SWT, 4>(A, st, route_only, hook);
+  if (A.T <= 8) return launch_decode_t<XT, WT, SWT, 8>(A, st, route_only, hook);
   return launch_decode_t<XT, WT, SWT, 16>(A, st, route_only, hook);
 }
 

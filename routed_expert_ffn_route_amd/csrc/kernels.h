@@ -20,8 +20,8 @@ struct LaunchHook {
   }
 };
 
-// Decode path (T <= kDecodeMaxT): stage 1 (router + shared gate/up + selection/plan),
-// routed gate/up, down + combine.  route_only stops after stage 1.
+// Decode path (T <= kDecodeMaxT): router, selection/plan + shared gate/up, routed gate/up,
+// down + combine (shared and routed).  route_only stops after the router.
 int launch_decode(Args A, hipStream_t st, bool route_only, const LaunchHook& hook);
 
 // Routing for any T: router logits (or logits_in), per-token selection, and the

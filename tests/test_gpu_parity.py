@@ -254,7 +254,17 @@ def test_ling_verify_window(orc, B, d):
     assert len(set(ids.ravel().tolist())) == d
 
 
-@pytest.mark.parametrize("T,d", [(1, None), (4, 32), (4, 20)])
+@pytest.mark.parametrize("T,d", [(2, 8), (2, 16), (3, 13), (3, 24), (5, 21), (5, 40)])
+def test_ling_verify_sweep(orc, B, T, d):
+    """Verify windows of 2, 3 and 5 tokens at the Ling shapes, each at the fewest and the most
+    distinct experts such a window can touch plus one value between."""
+    say(f"[ling-verify-sweep] T={T} d={d}")
+    Ld, xd = synth.device_layer(T, 2560, 512, 8, 768, 768, seed=300 + 10 * T + d, bias="verify", d=d)
+    y, ids = full_check(orc, B, None, None, Ld, xd, f"ling T={T} d={d}", copy_selected=True)
+    assert len(set(ids.ravel().tolist())) == d
+
+
+@pytest.mark.parametrize("T,d", [(1, None), (4, 32), (4, 20), (3, 17), (5, 33)])
 def test_ling_mxfp4(orc, B, T, d):
     """Ling shapes with MXFP4 experts (e2m1 codes, e8m0 scales 2^-4..2^2), bf16 activations
     and shared expert, fp32 output."""
