@@ -154,8 +154,9 @@ __device__ __forceinline__ void select_set_nv(const float* lrow, int E, int k, i
   ((uint4*)hist)[kWave + lane] = make_uint4(0u, 0u, 0u, 0u);
   uint32_t prefix = 0;
   int need = k;  // rank of the wanted key among the remaining candidates
-  int shift = 24;
-  for (int p = 0; p < 4; ++p, shift -= 8) {
+  int shift = 24;  // after the loop: the shift of the last digit taken (0 after all four)
+  for (int p = 0; p < 4; ++p) {
+    shift = 24 - 8 * p;
     unsigned* hp = hist + 256 * (p & 1);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll

@@ -154,6 +154,28 @@ def test_tiny_fp32_layer(orc, B):
     full_check(orc, B, Lh, xh, Ld, xd, "tiny")
 
 
+@pytest.mark.parametrize("T,H,E,k", [(1, 256, 256, 8), (4, 256, 512, 8), (3, 64, 100, 16),
+                                     (1, 64, 1024, 16), (8, 128, 64, 4), (2, 32, 7, 7)])
+def test_forward_exact_ties(orc, B, T, H, E, k):
+    """Router weights and activations in {-1, 0, 1} make every logit an exact integer, so many
+    tokens have equal logits at the k-th place; the forward pass must take the lower expert
+    index among equal logits, like the oracle, on every token (none is excused as a near tie)."""
+    say(f"[forward-ties] T={T} H={H} E={E} k={k}")
+    Lh, xh = synth.make_layer(T, H, E, k, 64, 64, seed=17 + E)
+    rng = np.random.default_rng(23 + T * E)
+    Lh.router_w = rng.integers(-1, 2, size=(E, H)).astype(np.float32)
+    xi = rng.integers(-1, 2, size=(T, H)).astype(np.float32)
+    xh = synth.f32_to_bf16_bits(xi) if Lh.act_dtype == "bf16" else xi
+    Ld, xd = synth.to_device(Lh, xh)
+    lg, ids, w = oracle_routing(orc, Lh, xh)
+    s = -np.sort(-lg, axis=1)
+    if k < E:
+        assert np.any(s[:, k - 1] == s[:, k]), "the draw has no tie at the k-th place"
+    y = y_host(Ld, forward_dev(B, Ld, xd))
+    ref = orc.forward_with_routing(Lh, xh, ids, w)
+    check_out(Lh, y, ref, f"ties T={T} E={E} k={k}")
+
+
 @pytest.mark.parametrize("T,H,E,k,tie", [
     (4, 256, 16, 2, False), (1, 2048, 256, 8, False), (4, 2560, 512, 8, False),
     (16, 256, 64, 8, True), (3, 64, 1024, 16, True), (5, 96, 7, 7, True), (1, 32, 1, 1, False),
