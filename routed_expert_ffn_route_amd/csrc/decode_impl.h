@@ -121,12 +121,50 @@ template <> struct GUC<MOE_MXFP4, MOE_BF16> {
   }
 };
 
+// Copying x rows into LDS: the block's threads take 16-byte units of the rows of the tokens in
+// `mask` (compacted: unit i lies in the (i / rw)-th token of the mask), kXB units per thread
+// per pass, all loads of a pass issued before any store (a load-store loop would wait a full
+// round trip per unit).
+constexpr int kXB = 4;
+__device__ __forceinline__ int nth_token(unsigned mask, int q) {
+  int t = 0;
+  for (;; ++t) {  // mask has more than q bits set
+    if ((mask >> t) & 1u) {
+      if (q == 0) return t;
+      --q;
+    }
+  }
+}
+__device__ __forceinline__ void x_rows_load(uint4 (&xr)[kXB], int base, int n, int rw, unsigned mask,
+                                            const uint8_t* xg, size_t xstride) {
+#pragma unroll
+  for (int j = 0; j < kXB; ++j) {
+    const int i = base + j * (int)blockDim.x;
+    if (i < n) {
+      const int q = i / rw, t = nth_token(mask, q);
+      xr[j] = ldg16(xg + (size_t)t * xstride + (size_t)(i - q * rw) * 16);
+    }
+  }
+}
+__device__ __forceinline__ void x_rows_store(const uint4 (&xr)[kXB], int base, int n, int rw,
+                                             unsigned mask, uint4* xs) {
+#pragma unroll
+  for (int j = 0; j < kXB; ++j) {
+    const int i = base + j * (int)blockDim.x;
+    if (i < n) {
+      const int q = i / rw, t = nth_token(mask, q);
+      xs[t * rw + (i - q * rw)] = xr[j];
+    }
+  }
+}
+
 // One lane group (G lanes) computes gate and up row `row` (reduction over K = H) for every
 // token in `mask` and writes out[slot][row] = silu(g) * u.  All loads of a K-slice are issued
 // before any is consumed; lanes past the row end load a valid chunk and scale it by 0.
-// XL: the block first copies the rows of x of the tokens in `mask` from xg into LDS at xs
-// (row t at t * xstride) -- after its first weight loads are in flight -- and reads x from
-// there; every thread of the block must call this function with the same mask.
+// XL: the block copies the rows of x of the tokens in `mask` from xg into LDS at xs (row t at
+// t * xstride) and reads x from there; the first pass of x loads is issued before the weight
+// loads, so that waiting for x does not wait for the weights.  Every thread of the block must
+// call this function with the same mask.
 template <int XT, int WT, int G, int NCH, int TM, bool XL>
 __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* urow,
                                            const uint8_t* gsrow, const uint8_t* usrow,
@@ -137,6 +175,9 @@ __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* u
   float ag[TM], au[TM];
 #pragma unroll
   for (int t = 0; t < TM; ++t) ag[t] = au[t] = 0.f;
+  uint4 xr[kXB];
+  const int rw = (int)(xstride / 16), xn = XL ? __popc(mask) * rw : 0;
+  if constexpr (XL) x_rows_load(xr, threadIdx.x, xn, rw, mask, xg, xstride);
   for (int c0 = 0; c0 < nchunks; c0 += G * NCH) {
     uint4 wg[NCH], wu[NCH];
     uint32_t bg[NCH], bu[NCH];  // e2m1: raw scale bytes, converted when the chunk is used
@@ -157,11 +198,10 @@ __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* u
     }
     if constexpr (XL) {
       if (c0 == 0) {  // the rows of the tokens in `mask` only
-        const int rw = (int)(xstride / 16);
-        for (int t = 0; t < TM; ++t) {
-          if (!((mask >> t) & 1u)) continue;  // uniform
-          for (int i = threadIdx.x; i < rw; i += blockDim.x)
-            xs[t * rw + i] = ldg16(xg + (size_t)t * xstride + (size_t)i * 16);
+        x_rows_store(xr, threadIdx.x, xn, rw, mask, xs);
+        for (int base = threadIdx.x + kXB * blockDim.x; base < xn; base += kXB * blockDim.x) {
+          x_rows_load(xr, base, xn, rw, mask, xg, xstride);
+          x_rows_store(xr, base, xn, rw, mask, xs);
         }
         __syncthreads();
       }
@@ -448,6 +488,25 @@ __global__ __launch_bounds__(kWave * TM) void dec_select(Args A, int nsh) {
   }
 }
 
+// Copies n 16-byte units from global memory to LDS with the whole block, B loads per thread
+// in flight before the first store.
+template <int B>
+__device__ __forceinline__ void stage16(uint4* dst, const uint4* src, int n) {
+  for (int base = threadIdx.x; base < n; base += B * blockDim.x) {
+    uint4 r[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = base + j * (int)blockDim.x;
+      if (i < n) r[j] = src[i];
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = base + j * (int)blockDim.x;
+      if (i < n) dst[i] = r[j];
+    }
+  }
+}
+
 // Streams np steps of a wave with two register buffers used in turn: step p + 1 is loaded
 // before step p is consumed, and no buffer is ever copied into the other (a register copy
 // would wait for the copied loads).  At the end the last step is loaded once more (cache-
@@ -537,11 +596,10 @@ __global__ __launch_bounds__(kThreads) void dec_gateup(Args A, int tiles, int sh
 // groups blockIdx.x, blockIdx.x + gridDim.x, ... and its NW waves share the work items round
 // robin: first (row group, K-slice) of the shared expert, then (row group, K-slice, distinct
 // expert) of the routed ones.  The plan and -- when they fit (ALDS) -- every routed and shared
-// activation row are staged in LDS once per block; a wave whose first item is a shared one
-// has that item's weights in flight before the staging barrier (they need no plan).  Each wave
-// streams its items' 16-byte weight chunks with the next item's loads in flight while it
-// consumes the current one.  Per (row group, wave) partial sums are added up in LDS and summed
-// over the waves in a fixed order at the end, so the result is deterministic.
+// activation row are staged in LDS once per block.  Each wave streams its items' 16-byte
+// weight chunks with the next item's loads in flight while it consumes the current one.  Per
+// (row group, wave) partial sums are added up in LDS and summed over the waves in a fixed
+// order at the end, so the result is deterministic.
 // Dynamic LDS (4-byte words): plan (2D + 2DT), partials [nrgb_max][NW][TM][RB], then ALDS
 // activations [T*k][I] at act_off and [T][Is] at ash_off.
 template <int WT, int SWT, int G, int NCH, int TM, bool ALDS>
@@ -672,10 +730,6 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
     }
   };
 
-  // this wave's items are q = wave + NW * step; a shared first item needs no plan
-  Buf a, b;
-  const bool pre = wave < nqs;  // uniform
-  if (pre) load(wave, a);
   nd = *P.nd();
   for (int i = threadIdx.x; i < D; i += blockDim.x) {
     s_e[i] = P.dexp()[i];
@@ -696,8 +750,9 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
   per_rg = nsl * nd;
   const int nq = nqs + nrgb * per_rg;
   const int nmine = wave < nq ? (nq - 1 - wave) / NW + 1 : 0;
-  if (nmine > 0) {  // uniform
-    if (!pre) load(wave, a);
+  if (nmine > 0) {  // uniform; this wave's items are q = wave + NW * step
+    Buf a, b;
+    load(wave, a);
     stream_loaded<Buf>(nmine, a, b, [&](int st, Buf& bf) { load(wave + NW * st, bf); },
                        [&](int st, const Buf& bf) { consume(wave + NW * st, bf); });
     flush();
