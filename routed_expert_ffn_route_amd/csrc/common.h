@@ -78,11 +78,9 @@ __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u &
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Round to nearest even; NaN stays NaN.
+// fp32 -> bf16, round to nearest even (NaN stays NaN): gfx950's v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // e8m0 scale byte -> fp32 power of two (0xFF -> NaN, 0x00 -> 2^-127 subnormal).  Branch

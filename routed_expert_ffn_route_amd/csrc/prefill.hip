@@ -19,6 +19,8 @@
 // All three GEMMs run one kernel, pf_gemm: 128 x 256 block tiles, K-steps of 32 staged in
 // a three-deep LDS ring that the buffer unit fills directly (loads to LDS, no register
 // staging), rows XOR-swizzled so that MFMA fragment reads are free of bank conflicts.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "select.h"
@@ -33,13 +35,24 @@ constexpr int kPfBN = 256;     // B rows per block (gate/up: 128 activation colu
 constexpr int kPfBK = 32;      // reduction step per LDS stage
 constexpr int kPfNS = 3;       // LDS ring depth (two 256-thread blocks per CU)
 
+// The router GEMM splits K over this many blocks per output tile when the tiles alone would
+// leave CUs idle (about 512 blocks wanted, at least four 32-deep K-steps per split); the
+// selection kernel adds the partial logits in split order.
+int pf_router_splits(int T, int H, int E) {
+  const int tiles = ((T + kPfBM - 1) / kPfBM) * ((E + 63) / 64);
+  const int want = (512 + tiles - 1) / tiles, most = std::max(1, H / kPfBK / 4);
+  return std::max(1, std::min(want, most));
+}
+
 size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is) {
   const size_t S = (size_t)T * k, R = S + T;
   const size_t Imax = I > Is ? I : Is;
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const int ks = pf_router_splits(T, H, E);
   return up(sizeof(int) * (E + 2)) * 2 + up(sizeof(int) * R) +
          up(sizeof(int) * 2 * (size_t)prefill_tiles_cap(T, E, k)) + up(256) + up(2 * R * Imax) +
-         up(2 * R * (size_t)H) + up(2 * 3 * (size_t)E * H);
+         up(2 * R * (size_t)H) + up(2 * 3 * (size_t)E * H) +
+         (ks > 1 ? up(sizeof(float) * (size_t)ks * T * E) : 0);
 }
 
 // Upper bound of sum over the E+1 groups of ceil(rows / kPfBM).
@@ -58,6 +71,8 @@ struct PfLayout {
   uint16_t* act;  // [S+T][Imax]
   uint16_t* out;  // [S+T][H]
   uint16_t* planes;  // [3][E][H] bf16 parts of the router weights
+  float* rpart;      // [ks][T][E] partial router logits (K split ks > 1 ways), else null
+  int ks;
 };
 
 PfLayout pf_layout(const Args& A) {
@@ -81,6 +96,9 @@ PfLayout pf_layout(const Args& A) {
   L.out = (uint16_t*)b;
   b += up(2 * R * (size_t)A.H);
   L.planes = (uint16_t*)b;
+  b += up(2 * 3 * (size_t)A.E * A.H);
+  L.ks = pf_router_splits(A.T, A.H, A.E);
+  L.rpart = L.ks > 1 ? (float*)b : nullptr;
   return L;
 }
 
@@ -193,7 +211,12 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
   const int nreal = MODE == 2 ? nblocks : min(nblocks, *L.ntiles * nb_per_tile);
   if ((int)blockIdx.x >= nreal) return;
   const int b = xcd_swizzle(blockIdx.x, nreal);
-  const int ti = b / nb_per_tile, nb = b - ti * nb_per_tile;
+  const int ti = b / nb_per_tile;
+  int nb = b - ti * nb_per_tile, ksp = 0;  // router: nb_per_tile counts (group, K split) pairs
+  if constexpr (MODE == 2) {
+    ksp = nb % L.ks;
+    nb /= L.ks;
+  }
   const int S = A.T * A.k;
   const size_t Imax = A.I > A.Is ? A.I : A.Is;
 
@@ -266,9 +289,12 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
     bo[j] = rowb == kOOB ? kOOB : rowb + c * 16u;
   }
 
-  const int nk = K / kPfBK;
+  // K-steps [s0, s0 + nk) of this block (the router may split K)
+  const int nk_all = K / kPfBK;
+  const int s0 = MODE == 2 ? ksp * nk_all / L.ks : 0;
+  const int nk = MODE == 2 ? (ksp + 1) * nk_all / L.ks - s0 : nk_all;
   auto issue = [&](int st, uint4* stage) {
-    const uint32_t kb = (uint32_t)(st < nk ? st : nk - 1) * kPfBK * 2u;
+    const uint32_t kb = (uint32_t)(s0 + (st < nk ? st : nk - 1)) * kPfBK * 2u;
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(ra, ao[j] + kb, lds_addr(stage + (wave * 2 + j) * 64));
 #pragma unroll
@@ -324,44 +350,77 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
   wait_vm<0>();  // no load may still write this block's LDS after it retires
 
   // ---- epilogue; C row = wm * 64 + m * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4
+  if constexpr (MODE == 2) {
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < 2; ++m) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
-      if (row >= nrows) continue;
-      if constexpr (MODE == 0) {
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const int col = n0 + wn * 64 + pr * 32 + (lane & 31);
-          if (col < N)
-            L.act[(size_t)(pos0 + row) * Imax + col] = f32_to_bf16(silu(acc[m][2 * pr][r]) * acc[m][2 * pr + 1][r]);
-        }
-      } else if constexpr (MODE == 1) {
-        const int slot = s_slot[row];
-        const float w = s_wt[row];
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const int h = n0 + wn * 128 + n * 32 + (lane & 31);
-          if (h < A.H) L.out[(size_t)slot * A.H + h] = f32_to_bf16(w * acc[m][n][r]);
-        }
-      } else {
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+        if (row >= nrows) continue;
         const int e = n0 + wn * 32 + (lane & 31), t = ti * BM + row;
         if (e < A.E) {
           float l = (acc[m][0][r] + acc[m][1][r]) + acc[m][2][r];
-          if (A.rbias) l += A.bias_stride == 0 ? bias_e : A.rbias[(size_t)t * A.bias_stride + e];
-          A.logits[(size_t)t * A.E + e] = l;
+          if (L.ks > 1) {  // partial over this K split; the selection kernel adds bias and parts
+            L.rpart[((size_t)ksp * A.T + t) * A.E + e] = l;
+          } else {
+            if (A.rbias) l += A.bias_stride == 0 ? bias_e : A.rbias[(size_t)t * A.bias_stride + e];
+            A.logits[(size_t)t * A.E + e] = l;
+          }
         }
       }
+    }
+  } else {
+    // The bf16 tile goes through LDS (the operand ring is free now), so that the global
+    // stores are whole 16-byte row pieces instead of one 2-byte element per lane.
+    constexpr int CW = MODE == 0 ? kPfBN / 2 : kPfBN;  // output columns of the tile
+    constexpr int LDW = CW + 8;                          // padded LDS row (bf16)
+    static_assert(BM * LDW * 2 <= NS * kStage * 16, "the output tile fits in the ring");
+    uint16_t* ct = (uint16_t*)smem;
+    __syncthreads();  // every wave is done with the ring
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+        if constexpr (MODE == 0) {
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr)
+            ct[row * LDW + wn * 64 + pr * 32 + (lane & 31)] =
+                f32_to_bf16(silu(acc[m][2 * pr][r]) * acc[m][2 * pr + 1][r]);
+        } else {
+          const float w = row < nrows ? s_wt[row] : 0.f;
+#pragma unroll
+          for (int n = 0; n < 4; ++n) ct[row * LDW + wn * 128 + n * 32 + (lane & 31)] = f32_to_bf16(w * acc[m][n][r]);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int UPR = CW / 8;  // 16-byte units per tile row
+    for (int u = tid; u < nrows * UPR; u += 2 * BM) {
+      const int row = u / UPR, cu = u - row * UPR, col = n0 + cu * 8;
+      if (col >= N) continue;
+      const uint4 v = *(const uint4*)&ct[row * LDW + cu * 8];
+      if constexpr (MODE == 0)
+        *(uint4*)&L.act[(size_t)(pos0 + row) * Imax + col] = v;
+      else
+        *(uint4*)&L.out[(size_t)s_slot[row] * A.H + col] = v;
     }
   }
 }
 
-__global__ __launch_bounds__(256) void pf_select(Args A) {
+__global__ __launch_bounds__(256) void pf_select(Args A, const float* rpart, int ks) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= A.T) return;
   const float* src = A.logits_in ? A.logits_in : A.logits;
+  if (rpart && !A.logits_in) {  // K-split router: logits = parts in split order + bias
+    for (int e = lane; e < A.E; e += 64) {
+      float l = rpart[(size_t)t * A.E + e];
+      for (int p = 1; p < ks; ++p) l += rpart[((size_t)p * A.T + t) * A.E + e];
+      if (A.rbias) l += A.rbias[(size_t)t * A.bias_stride + e];
+      A.logits[(size_t)t * A.E + e] = l;  // select_token reads back only what this lane wrote
+    }
+  }
   int* ids = A.ids + (size_t)t * A.k;
   float* w = A.cw + (size_t)t * A.k;
   select_token(src + (size_t)t * A.E, A.E, A.k, lane, ids, w);
@@ -418,14 +477,15 @@ int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook) {
     const PfLayout L = pf_layout(A);
     hook.pre("pf_router", st);
     pf_split_router<<<256, 256, 0, st>>>(A, L.planes);
-    const int nbt = (A.E + 63) / 64, tiles = (A.T + kPfBM - 1) / kPfBM;
+    const int nbt = ((A.E + 63) / 64) * L.ks, tiles = (A.T + kPfBM - 1) / kPfBM;
     const int nblocks = tiles * nbt;
     pf_gemm<2, kPfBM, kPfNS><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   }
+  const PfLayout L = pf_layout(A);
   hook.pre("pf_select", st);
-  pf_select<<<(A.T + 3) / 4, 256, 0, st>>>(A);
+  pf_select<<<(A.T + 3) / 4, 256, 0, st>>>(A, A.logits_in ? nullptr : L.rpart, L.ks);
   hook.post(st);
   if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
