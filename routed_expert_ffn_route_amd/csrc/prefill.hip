@@ -50,7 +50,7 @@ size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is) {
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
   const int ks = pf_router_splits(T, H, E);
   return up(sizeof(int) * (E + 2)) * 2 + up(sizeof(int) * R) +
-         up(sizeof(int) * 2 * (size_t)prefill_tiles_cap(T, E, k)) + up(256) + up(2 * R * Imax) +
+         up(sizeof(int) * 4 * (size_t)prefill_tiles_cap(T, E, k)) + up(256) + up(2 * R * Imax) +
          up(2 * R * (size_t)H) + up(2 * 3 * (size_t)E * H) +
          (ks > 1 ? up(sizeof(float) * (size_t)ks * T * E) : 0);
 }
@@ -66,7 +66,7 @@ struct PfLayout {
   int* count;   // [E+1]
   int* offset;  // [E+2]
   int* rows;    // [S+T]
-  int* tiles;   // [2*cap]
+  int* tiles;   // [cap] x {group, first row, rows, 0}
   int* ntiles;  // [1]
   uint16_t* act;  // [S+T][Imax]
   uint16_t* out;  // [S+T][H]
@@ -88,7 +88,7 @@ PfLayout pf_layout(const Args& A) {
   L.rows = (int*)b;
   b += up(sizeof(int) * R);
   L.tiles = (int*)b;
-  b += up(sizeof(int) * 2 * (size_t)prefill_tiles_cap(A.T, A.E, A.k));
+  b += up(sizeof(int) * 4 * (size_t)prefill_tiles_cap(A.T, A.E, A.k));
   L.ntiles = (int*)b;
   b += up(256);
   L.act = (uint16_t*)b;
@@ -100,6 +100,22 @@ PfLayout pf_layout(const Args& A) {
   L.ks = pf_router_splits(A.T, A.H, A.E);
   L.rpart = L.ks > 1 ? (float*)b : nullptr;
   return L;
+}
+
+// silu with the hardware exp and reciprocal (about 1 ulp each); its result is rounded to bf16.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// Lanes l, l^1 hold column c, c^1 of rows R (a) and R + 1 (b).  The even lane returns row R's
+// pair (c, c + 1) and the odd lane row R + 1's pair (c - 1, c), packed as two bf16.
+__device__ __forceinline__ uint32_t pair_pack(float a, float b, bool odd) {
+  const float send = odd ? a : b;
+  const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const f2 v = {odd ? recv : a, odd ? b : recv};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
 }
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -229,10 +245,10 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
     N = A.E;
   } else {
     if (ti >= *L.ntiles) return;
-    g = L.tiles[2 * ti];
-    const int it = L.tiles[2 * ti + 1];
-    nrows = min(BM, L.count[g] - it * BM);
-    pos0 = L.offset[g] + it * BM;
+    const int4 tl = ((const int4*)L.tiles)[ti];  // {group, first row, rows, 0}
+    g = tl.x;
+    pos0 = tl.y;
+    nrows = tl.z;
     K = MODE == 0 ? A.H : (g == A.E ? A.Is : A.I);
     N = MODE == 0 ? (g == A.E ? A.Is : A.I) : A.H;
   }
@@ -377,20 +393,28 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
     static_assert(BM * LDW * 2 <= NS * kStage * 16, "the output tile fits in the ring");
     uint16_t* ct = (uint16_t*)smem;
     __syncthreads();  // every wave is done with the ring
+    // A lane holds one column of rows R and R + 1 (r even, r + 1); lane pairs swap one value
+    // so that the even lane stores (R, c..c+1) and the odd lane (R + 1, c-1..c) as one dword.
+    const bool odd = lane & 1;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+      for (int r = 0; r < 16; r += 2) {
+        const int row0 = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+        const int row = row0 + (odd ? 1 : 0);
+        uint32_t* crow = (uint32_t*)(ct + row * LDW) + ((lane & 31) >> 1);
         if constexpr (MODE == 0) {
 #pragma unroll
-          for (int pr = 0; pr < 2; ++pr)
-            ct[row * LDW + wn * 64 + pr * 32 + (lane & 31)] =
-                f32_to_bf16(silu(acc[m][2 * pr][r]) * acc[m][2 * pr + 1][r]);
+          for (int pr = 0; pr < 2; ++pr) {
+            const float a = silu_fast(acc[m][2 * pr][r]) * acc[m][2 * pr + 1][r];
+            const float b = silu_fast(acc[m][2 * pr][r + 1]) * acc[m][2 * pr + 1][r + 1];
+            crow[(wn * 64 + pr * 32) / 2] = pair_pack(a, b, odd);
+          }
         } else {
-          const float w = row < nrows ? s_wt[row] : 0.f;
+          const float wa = row0 < nrows ? s_wt[row0] : 0.f, wb = row0 + 1 < nrows ? s_wt[row0 + 1] : 0.f;
 #pragma unroll
-          for (int n = 0; n < 4; ++n) ct[row * LDW + wn * 128 + n * 32 + (lane & 31)] = f32_to_bf16(w * acc[m][n][r]);
+          for (int n = 0; n < 4; ++n)
+            crow[(wn * 128 + n * 32) / 2] = pair_pack(wa * acc[m][n][r], wb * acc[m][n][r + 1], odd);
         }
       }
     }

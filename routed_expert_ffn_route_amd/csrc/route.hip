@@ -114,8 +114,8 @@ __device__ int wave_scan_lds(int* v, int n, int lane) {
 // Histogram -> exclusive scan -> scatter, in one 1024-thread block.  Groups are the E
 // experts plus, when with_shared, a final group E holding every token (the shared expert)
 // as rows S + t.  Writes counts [G], offsets [G+1], rows [S (+T)], and when tiles != null the
-// block map: for each group, ceil(count / bm) tiles (group, tile index), their number in
-// tiles_n.  The order inside a group is whatever the LDS atomics produce.
+// block map: for each group, ceil(count / bm) tiles {group, first row, rows, 0} (16 bytes
+// each), their number in tiles_n.  The order inside a group is whatever the LDS atomics produce.
 __global__ __launch_bounds__(1024) void permute(const int* ids, int T, int k, int E, bool with_shared,
                                                 int* counts, int* offsets, int* rows, int* tiles,
                                                 int* tiles_n, int bm) {
@@ -155,10 +155,8 @@ __global__ __launch_bounds__(1024) void permute(const int* ids, int T, int k, in
   if (tiles) {
     for (int g = tid; g < G; g += 1024) {
       const int nt = (s_cnt[g] + bm - 1) / bm;
-      for (int i = 0; i < nt; ++i) {
-        tiles[2 * (s_til[g] + i)] = g;
-        tiles[2 * (s_til[g] + i) + 1] = i;
-      }
+      for (int i = 0; i < nt; ++i)
+        ((int4*)tiles)[s_til[g] + i] = make_int4(g, s_off[g] + i * bm, min(bm, s_cnt[g] - i * bm), 0);
     }
   }
   __syncthreads();
