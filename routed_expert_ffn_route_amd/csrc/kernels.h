@@ -28,6 +28,12 @@ int launch_decode(Args A, hipStream_t st, bool route_only, const LaunchHook& hoo
 // histogram / scan / scatter plan written to the moe_route outputs.
 int launch_route_any(Args A, hipStream_t st, bool decode_sized, const LaunchHook& hook);
 
+// Token-to-expert permutation over many blocks (count, plan, scatter) for the forward pass;
+// bcnt: workspace of permute_blocks(T, k) * E ints.
+int permute_blocks(int T, int k);
+int launch_permute_many(const int* ids, int T, int k, int E, bool with_shared, int* bcnt, int* counts,
+                        int* offsets, int* rows, int* tiles, int* tiles_n, int bm, hipStream_t st);
+
 // Router (MFMA, bf16 activations) + selection for T > kDecodeMaxT.
 int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook);
 

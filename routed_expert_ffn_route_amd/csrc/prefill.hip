@@ -52,7 +52,8 @@ size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is) {
   return up(sizeof(int) * (E + 2)) * 2 + up(sizeof(int) * R) +
          up(sizeof(int) * 4 * (size_t)prefill_tiles_cap(T, E, k)) + up(256) + up(2 * R * Imax) +
          up(2 * R * (size_t)H) + up(2 * 3 * (size_t)E * H) +
-         (ks > 1 ? up(sizeof(float) * (size_t)ks * T * E) : 0);
+         (ks > 1 ? up(sizeof(float) * (size_t)ks * T * E) : 0) +
+         up(sizeof(int) * (size_t)permute_blocks(T, k) * E);
 }
 
 // Upper bound of sum over the E+1 groups of ceil(rows / kPfBM).
@@ -73,6 +74,7 @@ struct PfLayout {
   uint16_t* planes;  // [3][E][H] bf16 parts of the router weights
   float* rpart;      // [ks][T][E] partial router logits (K split ks > 1 ways), else null
   int ks;
+  int* bcnt;         // [permute_blocks][E] per-block expert counts of the permutation
 };
 
 PfLayout pf_layout(const Args& A) {
@@ -99,6 +101,8 @@ PfLayout pf_layout(const Args& A) {
   b += up(2 * 3 * (size_t)A.E * A.H);
   L.ks = pf_router_splits(A.T, A.H, A.E);
   L.rpart = L.ks > 1 ? (float*)b : nullptr;
+  if (L.ks > 1) b += up(sizeof(float) * (size_t)L.ks * A.T * A.E);
+  L.bcnt = (int*)b;
   return L;
 }
 
@@ -489,10 +493,6 @@ __global__ __launch_bounds__(256) void pf_combine(Args A, PfLayout L) {
 
 }  // namespace
 
-__global__ __launch_bounds__(1024) void permute(const int* ids, int T, int k, int E, bool with_shared,
-                                                int* counts, int* offsets, int* rows, int* tiles,
-                                                int* tiles_n, int bm);
-
 // Router logits + per-token selection for T > 16 with bf16 activations (also used by
 // moe_route so that routing-only calls take the forward path's arithmetic).
 int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook) {
@@ -521,10 +521,10 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   int rc = launch_pf_route(A, st, hook);
   if (rc) return rc;
   hook.pre("pf_permute", st);
-  permute<<<1, 1024, 0, st>>>(A.ids, A.T, A.k, A.E, A.Is > 0, L.count, L.offset, L.rows, L.tiles,
-                              L.ntiles, kPfBM);
+  rc = launch_permute_many(A.ids, A.T, A.k, A.E, A.Is > 0, L.bcnt, L.count, L.offset, L.rows, L.tiles,
+                           L.ntiles, kPfBM, st);
   hook.post(st);
-  if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
+  if (rc) return rc;
   const int cap = prefill_tiles_cap(A.T, A.E, A.k);
   const int Imax = A.I > A.Is ? A.I : A.Is;
   {

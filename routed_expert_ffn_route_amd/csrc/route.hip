@@ -173,6 +173,97 @@ __global__ __launch_bounds__(1024) void permute(const int* ids, int T, int k, in
   }
 }
 
+// The same permutation over many blocks, for the forward pass's large T: the assignments are
+// cut into chunks of kPermChunk; (1) each block counts its chunk's experts in LDS and writes
+// its counts per expert, (2) one block adds them up per expert, turns each block's count into
+// its start inside the expert's group (a prefix over blocks), scans the group sizes into
+// offsets and writes the block map, (3) each block scatters its chunk from those starts with
+// LDS cursors.  bcnt: [nblocks][E] ints of workspace.
+constexpr int kPermChunk = 512;
+__global__ __launch_bounds__(256) void permute_count(const int* ids, int S, int E, int* bcnt) {
+  __shared__ int s_h[MOE_MAX_E];
+  for (int g = threadIdx.x; g < E; g += blockDim.x) s_h[g] = 0;
+  __syncthreads();
+  const int s0 = blockIdx.x * kPermChunk, s1 = min(S, s0 + kPermChunk);
+  for (int s = s0 + threadIdx.x; s < s1; s += blockDim.x) atomicAdd(&s_h[ids[s]], 1);
+  __syncthreads();
+  for (int g = threadIdx.x; g < E; g += blockDim.x) bcnt[(size_t)blockIdx.x * E + g] = s_h[g];
+}
+
+__global__ __launch_bounds__(1024) void permute_plan(int* bcnt, int nb, int T, int k, int E, bool with_shared,
+                                                     int* counts, int* offsets, int* rows, int* tiles,
+                                                     int* tiles_n, int bm) {
+  __shared__ int s_cnt[MOE_MAX_E + 2];
+  __shared__ int s_off[MOE_MAX_E + 2];
+  __shared__ int s_til[MOE_MAX_E + 2];
+  __shared__ int s_total, s_ntiles;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int S = T * k, G = E + (with_shared ? 1 : 0);
+  constexpr int kB = 16;  // counts read per pass before any is overwritten (one round trip)
+  for (int g = tid; g < E; g += blockDim.x) {  // per expert: prefix over the blocks
+    int run = 0;
+    for (int b0 = 0; b0 < nb; b0 += kB) {
+      int c[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) c[j] = b0 + j < nb ? bcnt[(size_t)(b0 + j) * E + g] : 0;
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        if (b0 + j < nb) bcnt[(size_t)(b0 + j) * E + g] = run;
+        run += c[j];
+      }
+    }
+    s_cnt[g] = run;
+  }
+  if (tid == 0 && with_shared) s_cnt[E] = T;
+  __syncthreads();
+  for (int g = tid; g < G; g += blockDim.x) {
+    s_off[g] = s_cnt[g];
+    s_til[g] = (s_cnt[g] + bm - 1) / bm;
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const int tot = wave_scan_lds(s_off, G, lane);
+    if (lane == 0) s_total = tot;
+  } else if (tid < 2 * kWave) {
+    const int tot = wave_scan_lds(s_til, G, lane);
+    if (lane == 0) s_ntiles = tot;
+  }
+  __syncthreads();
+  for (int g = tid; g < G; g += blockDim.x) {
+    counts[g] = s_cnt[g];
+    offsets[g] = s_off[g];
+    const int nt = (s_cnt[g] + bm - 1) / bm;
+    for (int i = 0; i < nt; ++i)
+      ((int4*)tiles)[s_til[g] + i] = make_int4(g, s_off[g] + i * bm, min(bm, s_cnt[g] - i * bm), 0);
+  }
+  if (tid == 0) {
+    offsets[G] = s_total;
+    *tiles_n = s_ntiles;
+  }
+  if (with_shared)
+    for (int t = tid; t < T; t += blockDim.x) rows[s_off[E] + t] = S + t;
+}
+
+__global__ __launch_bounds__(256) void permute_scatter(const int* ids, int S, int E, const int* bcnt,
+                                                       const int* offsets, int* rows) {
+  __shared__ int s_cur[MOE_MAX_E];
+  for (int g = threadIdx.x; g < E; g += blockDim.x) s_cur[g] = offsets[g] + bcnt[(size_t)blockIdx.x * E + g];
+  __syncthreads();
+  const int s0 = blockIdx.x * kPermChunk, s1 = min(S, s0 + kPermChunk);
+  for (int s = s0 + threadIdx.x; s < s1; s += blockDim.x) rows[atomicAdd(&s_cur[ids[s]], 1)] = s;
+}
+
+int permute_blocks(int T, int k) { return (T * k + kPermChunk - 1) / kPermChunk; }
+
+int launch_permute_many(const int* ids, int T, int k, int E, bool with_shared, int* bcnt, int* counts,
+                        int* offsets, int* rows, int* tiles, int* tiles_n, int bm, hipStream_t st) {
+  const int S = T * k, nb = permute_blocks(T, k);
+  permute_count<<<nb, 256, 0, st>>>(ids, S, E, bcnt);
+  permute_plan<<<1, 1024, 0, st>>>(bcnt, nb, T, k, E, with_shared, counts, offsets, rows, tiles, tiles_n, bm);
+  permute_scatter<<<nb, 256, 0, st>>>(ids, S, E, bcnt, offsets, rows);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
 int launch_route_any(Args A, hipStream_t st, bool decode_sized, const LaunchHook& hook) {
   hipError_t err;
   if (!decode_sized && A.act == MOE_BF16) {  // the prefill path's router and selection
