@@ -6,7 +6,8 @@ with Qwen-style shapes: T=1, hidden 2048, 256 routed experts top-8 + 1 shared, e
 shared intermediate 512, bf16 weights and activations, fp32 router; 48 independently drawn
 layers are rotated call by call so that no layer's weights stay in the 256 MiB Infinity
 Cache.  Other workloads (--workload): ling_verify (T=4, H=2560, E=512, I=768, d distinct
-experts), ling_mxfp4 (same with MXFP4 experts; T=1 or 4), qwen_prefill (T=4096).
+experts), ling_mxfp4 (same with MXFP4 experts; T=1 or 4), qwen_prefill (T=4096),
+ling_mxfp4_prefill (T=4096, Ling shapes, MXFP4 experts, Zipf expert load).
 
 Prints ONE JSON line: value = tokens/s of the whole layer (inputs resident in HBM), the
 roofline of the dominant kernel (its algorithmic bytes per launch over its mean launch time
@@ -39,6 +40,9 @@ def workload_spec(name, T_override=None, d=32):
         return dict(T=T, H=2560, E=512, k=8, I=768, I_shared=768, act="bf16", expert="mxfp4",
                     shared="bf16", out="f32", bias=("verify" if T > 1 else None), d=(d if T > 1 else None),
                     layers=48)
+    if name == "ling_mxfp4_prefill":
+        return dict(T=T_override or 4096, H=2560, E=512, k=8, I=768, I_shared=768, act="bf16", expert="mxfp4",
+                    shared="bf16", out="f32", bias="zipf", d=None, layers=8)
     if name == "qwen_prefill":
         return dict(T=T_override or 4096, H=2048, E=256, k=8, I=512, I_shared=512, act="bf16", expert="bf16",
                     shared="bf16", out="bf16", bias="zipf", d=None, layers=8)

@@ -66,7 +66,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype_t;
 #define MOE_MAX_K 16       /* experts per token                                */
 #define MOE_MAX_H 16384    /* hidden size                                      */
 #define MOE_MAX_I 8192     /* intermediate sizes                               */
-/* T > 16 (grouped-GEMM path) additionally needs T * H * 2 < 2^31 bytes of x. */
+/* T > 16 (grouped-GEMM path) additionally needs bf16 activations, T * H * 2 < 2^31 bytes
+   of x and, with MXFP4 experts, H <= 8192 and I <= 8192 (a tile's scale rows sit in LDS). */
 
 typedef struct {
   int32_t T;            /* tokens, >= 1                                        */

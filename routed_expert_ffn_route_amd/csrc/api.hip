@@ -35,7 +35,9 @@ int check_shape(const moe_shape_t* s) {
   if (!f32 && !b16) return MOE_EUNSUPPORTED;
   if (s->out_dtype != MOE_F32 && s->out_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
   if (s->T > kDecodeMaxT) {  // prefill path
-    if (s->act_dtype != MOE_BF16 || s->expert_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+    if (s->act_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+    // MXFP4 experts: the scale rows of a 256-row weight tile are staged in LDS (K / 32 <= 256)
+    if (s->expert_dtype == MOE_MXFP4 && (s->H > 8192 || s->I > 8192)) return MOE_EUNSUPPORTED;
     if ((size_t)s->T * s->H * 2 >= ((size_t)1 << 31)) return MOE_EUNSUPPORTED;  // 32-bit row offsets
   }
   return MOE_OK;

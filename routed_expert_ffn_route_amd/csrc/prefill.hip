@@ -218,21 +218,29 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int MODE, int BM, int NS>
-__global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks) {
-  constexpr int kStage = (BM + kPfBN) * kPfBK * 2 / 16;  // 16-byte units per stage
-  constexpr int kNB = 512 / BM;                           // B load instructions per wave per step
-  __shared__ __attribute__((aligned(16))) uint4 smem[NS * kStage];
+template <int MODE, int BM, int NS, int WT>
+__global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks,
+                                                                     int part) {
+  constexpr bool F4 = WT == MOE_MXFP4;
+  constexpr int kStageA = BM * kPfBK * 2 / 16;                    // 16-byte units per stage
+  constexpr int kStage = kStageA + (F4 ? kPfBN : kPfBN * kPfBK * 2 / 16);
+  constexpr int kNB = F4 ? 1 : 512 / BM;                          // B load instructions per wave per step
+  extern __shared__ __attribute__((aligned(16))) uint4 smem_dyn[];
+  __shared__ __attribute__((aligned(16))) uint4 smem_st[F4 ? 1 : NS * kStage];
+  uint4* smem = F4 ? smem_dyn : smem_st;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   // the grouped GEMMs' real blocks are the first ntiles * nb_per_tile (the grid is sized for
-  // the worst case); the rest leave at once
-  const int nreal = MODE == 2 ? nblocks : min(nblocks, *L.ntiles * nb_per_tile);
+  // the worst case); the rest leave at once.  part 1: the routed groups' tiles only, part 2:
+  // the shared expert's tiles only (the last ceil(T / BM) of the map).
+  const int shtiles = A.Is > 0 ? (A.T + BM - 1) / BM : 0;
+  const int ntl = MODE == 2 ? 0 : *L.ntiles - (part == 1 ? shtiles : 0);
+  const int nreal = MODE == 2 || part == 2 ? nblocks : min(nblocks, ntl * nb_per_tile);
   if ((int)blockIdx.x >= nreal) return;
   const int b = xcd_swizzle(blockIdx.x, nreal);
-  const int ti = b / nb_per_tile;
-  int nb = b - ti * nb_per_tile, ksp = 0;  // router: nb_per_tile counts (group, K split) pairs
+  const int tb = b / nb_per_tile, ti = tb + (part == 2 ? *L.ntiles - shtiles : 0);
+  int nb = b - tb * nb_per_tile, ksp = 0;  // router: nb_per_tile counts (group, K split) pairs
   if constexpr (MODE == 2) {
     ksp = nb % L.ks;
     nb /= L.ks;
@@ -282,25 +290,56 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
     }
     ao[j] = rowb == kOOB ? kOOB : rowb + c * 16u;
   }
+  // MXFP4 B: row r of the tile is lane r % 64 of wave r / 64, one 16-byte chunk (32 codes) per
+  // step.  The e8m0 scales (sb = K / 32 bytes per row) of a wave's 64 rows are one contiguous
+  // block of the scale matrix, 16-byte aligned (64 sb is a multiple of 16), staged in LDS for
+  // the whole tile at wstr bytes per wave.
+  const int sb = F4 ? K / 32 : 0, sbi = (64 * sb + 1023) / 1024, wstr = sbi * 1024;
+  i32x4_t rs;
+  uint32_t so = kOOB;  // the wave's first scale row's offset (uniform)
 #pragma unroll
   for (int j = 0; j < kNB; ++j) {
-    // instruction j of this wave covers B rows 16 (kNB wave + j) ... + 15
-    const int p = (wave * kNB + j) * 64 + lane, r = p >> 2, c = (p & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
+    // bf16: instruction j of this wave covers B rows 16 (kNB wave + j) ... + 15
+    int r, c;
+    if constexpr (F4) {
+      r = wave * 64 + lane;
+      c = 0;
+    } else {
+      const int p = (wave * kNB + j) * 64 + lane;
+      r = p >> 2;
+      c = (p & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
+    }
     const int half = r >> 7, jj = r & 127;
     uint32_t rowb = kOOB;
     if constexpr (MODE == 0) {
-      const bool up = (jj >> 5) & 1;  // uniform per instruction
+      // rows 64 half + 0..63 gate, 64 half + 64..127 up, of columns n0 + 64 half ... + 63
+      const bool up = jj >> 6;  // uniform per instruction
       const bool sh = g == A.E;
-      const uint16_t* base = up ? (sh ? (const uint16_t*)A.sup : (const uint16_t*)A.up + (size_t)g * A.I * A.H)
-                                : (sh ? (const uint16_t*)A.sgate : (const uint16_t*)A.gate + (size_t)g * A.I * A.H);
-      rb[j] = buf_rsrc(base, (size_t)N * A.H * 2);
-      const int col = n0 + half * 64 + (jj >> 6) * 32 + (jj & 31);
-      if (col < N) rowb = (uint32_t)col * A.H * 2u;
+      const int col = n0 + half * 64 + (jj & 63);
+      if constexpr (F4) {
+        const uint8_t* base = (const uint8_t*)(up ? A.up : A.gate) + (size_t)g * A.I * (A.H / 2);
+        rb[j] = buf_rsrc(base, (size_t)N * (A.H / 2));
+        if (col < N) rowb = (uint32_t)col * (A.H / 2);
+        rs = buf_rsrc((up ? A.us : A.gs) + (size_t)g * A.I * (A.H / 32), (size_t)N * (A.H / 32));
+        so = (uint32_t)(n0 + half * 64) * (A.H / 32);
+      } else {
+        const uint16_t* base = up ? (sh ? (const uint16_t*)A.sup : (const uint16_t*)A.up + (size_t)g * A.I * A.H)
+                                  : (sh ? (const uint16_t*)A.sgate : (const uint16_t*)A.gate + (size_t)g * A.I * A.H);
+        rb[j] = buf_rsrc(base, (size_t)N * A.H * 2);
+        if (col < N) rowb = (uint32_t)col * A.H * 2u;
+      }
     } else if constexpr (MODE == 1) {
-      const uint16_t* base = g == A.E ? (const uint16_t*)A.sdown : (const uint16_t*)A.down + (size_t)g * A.H * A.I;
-      rb[j] = buf_rsrc(base, (size_t)A.H * K * 2);
       const int h = n0 + r;
-      if (h < A.H) rowb = (uint32_t)h * K * 2u;
+      if constexpr (F4) {
+        rb[j] = buf_rsrc((const uint8_t*)A.down + (size_t)g * A.H * (A.I / 2), (size_t)A.H * (K / 2));
+        if (h < A.H) rowb = (uint32_t)h * (K / 2);
+        rs = buf_rsrc(A.ds + (size_t)g * A.H * (A.I / 32), (size_t)A.H * (K / 32));
+        so = (uint32_t)(n0 + wave * 64) * (K / 32);
+      } else {
+        const uint16_t* base = g == A.E ? (const uint16_t*)A.sdown : (const uint16_t*)A.down + (size_t)g * A.H * A.I;
+        rb[j] = buf_rsrc(base, (size_t)A.H * K * 2);
+        if (h < A.H) rowb = (uint32_t)h * K * 2u;
+      }
     } else {
       rb[j] = buf_rsrc(L.planes, (size_t)3 * A.E * A.H * 2);
       const int plane = jj >> 5, e = n0 + half * 32 + (jj & 31);
@@ -314,12 +353,20 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
   const int s0 = MODE == 2 ? ksp * nk_all / L.ks : 0;
   const int nk = MODE == 2 ? (ksp + 1) * nk_all / L.ks - s0 : nk_all;
   auto issue = [&](int st, uint4* stage) {
-    const uint32_t kb = (uint32_t)(s0 + (st < nk ? st : nk - 1)) * kPfBK * 2u;
+    const uint32_t ks = (uint32_t)(s0 + (st < nk ? st : nk - 1));
+    const uint32_t kb = ks * kPfBK * 2u, kbb = F4 ? ks * 16u : kb;
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(ra, ao[j] + kb, lds_addr(stage + (wave * 2 + j) * 64));
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) dma16(rb[j], bo[j] + kb, lds_addr(stage + BM * 4 + (wave * kNB + j) * 64));
+    for (int j = 0; j < kNB; ++j) dma16(rb[j], bo[j] + kbb, lds_addr(stage + kStageA + (wave * kNB + j) * 64));
   };
+  // MXFP4: the tile's scale rows, wave w's 64 rows by wave w, before the first stages (so the
+  // first stage's wait covers them); they sit after the ring
+  uint8_t* s_sc = (uint8_t*)(smem + NS * kStage);
+  if constexpr (F4) {
+    for (int i = 0; i < sbi; ++i)
+      dma16(rs, so + (uint32_t)(i * 64 + lane) * 16u, lds_addr((uint4*)(s_sc + (size_t)wave * wstr) + i * 64));
+  }
 
   // down: the tile's slots and routing weights, staged in LDS while the operands stream
   __shared__ int s_slot[BM];
@@ -354,8 +401,21 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
       for (int m = 0; m < 2; ++m)
         af[m] = __builtin_bit_cast(bf16x8_t, st[swz_unit(wm * 64 + m * 32 + (lane & 31), c)]);
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
-        bfr[n] = __builtin_bit_cast(bf16x8_t, st[BM * 4 + swz_unit(wn * 128 + n * 32 + (lane & 31), c)]);
+      for (int n = 0; n < 4; ++n) {
+        const int br = wn * 128 + n * 32 + (lane & 31);
+        if constexpr (F4) {  // 8 codes of this lane's K range, scaled while unpacked to bf16
+          const uint32_t q = ((const uint32_t*)(st + kStageA + br))[c];
+          const float sc = e8m0_to_f32(s_sc[(br >> 6) * wstr + (br & 63) * sb + s0 + s]);
+          uint32_t v[4];
+          v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 0));
+          v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1));
+          v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 2));
+          v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 3));
+          bfr[n] = __builtin_bit_cast(bf16x8_t, make_uint4(v[0], v[1], v[2], v[3]));
+        } else {
+          bfr[n] = __builtin_bit_cast(bf16x8_t, st[kStageA + swz_unit(br, c)]);
+        }
+      }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         if (m >= mlive) break;  // uniform
@@ -394,7 +454,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
     // stores are whole 16-byte row pieces instead of one 2-byte element per lane.
     constexpr int CW = MODE == 0 ? kPfBN / 2 : kPfBN;  // output columns of the tile
     constexpr int LDW = CW + 8;                          // padded LDS row (bf16)
-    static_assert(BM * LDW * 2 <= NS * kStage * 16, "the output tile fits in the ring");
+    static_assert(F4 || BM * LDW * 2 <= NS * kStage * 16, "the output tile fits in the ring");
     uint16_t* ct = (uint16_t*)smem;
     __syncthreads();  // every wave is done with the ring
     // A lane holds one column of rows R and R + 1 (r even, r + 1); lane pairs swap one value
@@ -410,8 +470,8 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
         if constexpr (MODE == 0) {
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr) {
-            const float a = silu_fast(acc[m][2 * pr][r]) * acc[m][2 * pr + 1][r];
-            const float b = silu_fast(acc[m][2 * pr][r + 1]) * acc[m][2 * pr + 1][r + 1];
+            const float a = silu_fast(acc[m][pr][r]) * acc[m][2 + pr][r];
+            const float b = silu_fast(acc[m][pr][r + 1]) * acc[m][2 + pr][r + 1];
             crow[(wn * 64 + pr * 32) / 2] = pair_pack(a, b, odd);
           }
         } else {
@@ -503,7 +563,7 @@ int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook) {
     pf_split_router<<<256, 256, 0, st>>>(A, L.planes);
     const int nbt = ((A.E + 63) / 64) * L.ks, tiles = (A.T + kPfBM - 1) / kPfBM;
     const int nblocks = tiles * nbt;
-    pf_gemm<2, kPfBM, kPfNS><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks);
+    pf_gemm<2, kPfBM, kPfNS, MOE_BF16><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks, 0);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   }
@@ -527,21 +587,46 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   if (rc) return rc;
   const int cap = prefill_tiles_cap(A.T, A.E, A.k);
   const int Imax = A.I > A.Is ? A.I : A.Is;
+  const bool f4 = A.wdt == MOE_MXFP4;
+  // MXFP4 experts: the routed groups' tiles run the MXFP4 kernel (dynamic LDS: ring, scale
+  // rows, or the output tile if larger), the shared expert's tiles the bf16 kernel
+  auto f4_lds = [&](int mode, int K) {
+    const size_t ring = (size_t)kPfNS * (kPfBM * kPfBK * 2 + kPfBN * 16);
+    const size_t sc = (size_t)4 * ((64 * (K / 32) + 1023) / 1024) * 1024;  // four waves' scale blocks
+    const size_t epi = (size_t)kPfBM * ((mode == 0 ? kPfBN / 2 : kPfBN) + 8) * 2;
+    return std::max(ring + sc, epi);
+  };
+  auto run = [&](const void* f, int nblocks, int nbt, int part, size_t lds) -> int {
+    if (lds > 65536 && hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return MOE_EHIP;
+    PfLayout Lc = L;
+    void* args[] = {&A, &Lc, &nbt, &nblocks, &part};
+    return hipLaunchKernel(f, dim3(nblocks), dim3(2 * kPfBM), args, lds, st) == hipSuccess ? MOE_OK : MOE_EHIP;
+  };
+  const int shtiles = A.Is > 0 ? (A.T + kPfBM - 1) / kPfBM : 0;
   {
     const int nbt = (Imax + kPfBN / 2 - 1) / (kPfBN / 2);
-    const int nblocks = cap * nbt;
     hook.pre("pf_gateup", st);
-    pf_gemm<0, kPfBM, kPfNS><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks);
+    if (!f4) {
+      rc = run((const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16>, cap * nbt, nbt, 0, 0);
+    } else {
+      rc = run((const void*)pf_gemm<0, kPfBM, kPfNS, MOE_MXFP4>, cap * nbt, nbt, 1, f4_lds(0, A.H));
+      if (!rc && shtiles) rc = run((const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16>, shtiles * nbt, nbt, 2, 0);
+    }
     hook.post(st);
-    if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
+    if (rc) return rc;
   }
   {
     const int nbt = (A.H + kPfBN - 1) / kPfBN;
-    const int nblocks = cap * nbt;
     hook.pre("pf_down", st);
-    pf_gemm<1, kPfBM, kPfNS><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks);
+    if (!f4) {
+      rc = run((const void*)pf_gemm<1, kPfBM, kPfNS, MOE_BF16>, cap * nbt, nbt, 0, 0);
+    } else {
+      rc = run((const void*)pf_gemm<1, kPfBM, kPfNS, MOE_MXFP4>, cap * nbt, nbt, 1, f4_lds(1, A.I));
+      if (!rc && shtiles) rc = run((const void*)pf_gemm<1, kPfBM, kPfNS, MOE_BF16>, shtiles * nbt, nbt, 2, 0);
+    }
     hook.post(st);
-    if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
+    if (rc) return rc;
   }
   hook.pre("pf_combine", st);
   pf_combine<<<(unsigned)(((size_t)A.T * (A.H / 8) + 255) / 256), 256, 0, st>>>(A, L);

@@ -8,7 +8,8 @@ Bars (floating point compared with the oracle's double-precision result):
     is below 1e-5, where either order is accepted;
   * bf16 output: max relative error <= 2e-2 (|y - y_ref| / max(|y_ref|, rms(y_ref))) and
     relative L2 <= 5e-3;
-  * MXFP4 experts with fp32 output: relative L2 <= 1e-3;
+  * MXFP4 experts with fp32 output: relative L2 <= 1e-3 on the decode path (T <= 16); on the
+    grouped-GEMM path (T > 16) the MFMAs take bf16 activations, so the bf16 bars apply;
   * all-fp32 layer: relative L2 <= 1e-5 (fp32 accumulation over <= 2^12 terms stays
     near 1e-6).
 """
@@ -62,8 +63,10 @@ def check_out(L, y, ref, tag):
     max_rel, l2 = errs(y, ref)
     say(f"[{tag}] max_rel={max_rel:.3e} rel_l2={l2:.3e}")
     assert np.all(np.isfinite(y)), tag
-    if L.expert_dtype == "mxfp4":
+    if L.expert_dtype == "mxfp4" and L.T <= 16:
         assert l2 <= 1e-3, tag
+    elif L.expert_dtype == "mxfp4":  # grouped-GEMM path: bf16 activations feed the MFMAs
+        assert max_rel <= 2e-2 and l2 <= 5e-3, tag
     elif L.out_dtype == "bf16":
         assert max_rel <= 2e-2 and l2 <= 5e-3, tag
     elif L.act_dtype == "f32" and L.expert_dtype == "f32":
@@ -346,6 +349,51 @@ def test_prefill_f32_out(orc, B):
     Lh, xh = synth.make_layer(40, 256, 16, 4, 64, 64, out="f32", seed=8)
     Ld, xd = synth.to_device(Lh, xh)
     full_check(orc, B, Lh, xh, Ld, xd, "prefill f32out")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=17, H=256, E=16, k=2, I=128, I_shared=128),
+    dict(T=64, H=512, E=32, k=4, I=192, I_shared=64, bias="zipf"),   # ragged tiles, 6 scales per row
+    dict(T=300, H=1024, E=64, k=8, I=512, I_shared=512, bias="zipf"),
+    dict(T=200, H=96, E=8, k=2, I=96, I_shared=0),                    # no shared expert
+    dict(T=129, H=2560, E=64, k=8, I=768, I_shared=768),              # Ling widths
+])
+def test_prefill_small_mxfp4(orc, B, kw):
+    """MXFP4 experts on the grouped-GEMM path: codes and scales unpacked to bf16 on the way
+    from LDS into the MFMA; the shared expert (bf16) takes the bf16 kernel."""
+    say(f"[prefill-mxfp4] {kw}")
+    Lh, xh = synth.make_layer(**kw, act="bf16", expert="mxfp4", shared="bf16", out="f32", seed=9)
+    Ld, xd = synth.to_device(Lh, xh)
+    assert B.path_name(B.shape_of(Ld)) == "prefill.mxfp4"
+    full_check(orc, B, Lh, xh, Ld, xd, f"prefill-mxfp4 {kw}")
+
+
+def test_ling_mxfp4_prefill_full_size_sampled(orc, B):
+    """Ling-shaped MXFP4 prefill (T=4096, 512 experts top-8, Zipf(1.1) bias) at full size in
+    the benchmark's launch configuration; the oracle checks a sample of tokens."""
+    import torch
+    say("[ling-mxfp4-prefill] T=4096")
+    Ld, xd = synth.device_layer(4096, 2560, 512, 8, 768, 768, "bf16", "mxfp4", "bf16", "f32", seed=3,
+                                bias="zipf")
+    y = y_host(Ld, forward_dev(B, Ld, xd))
+    r = B.layer_route(Ld, xd)
+    torch.cuda.synchronize()
+    gids = r["ids"].cpu().numpy()
+    counts = r["count"].cpu().numpy()
+    assert counts.sum() == 4096 * 8
+    hot = int(np.argmax(counts))
+    rng = np.random.default_rng(1)
+    pick = sorted(set(rng.choice(4096, 24, replace=False).tolist()) |
+                  set(np.nonzero((gids == hot).any(axis=1))[0][:8].tolist()) | {0, 4095})
+    Lh, xh = host_view_for_oracle(Ld, xd, ids_needed=gids[pick].ravel())
+    sub = Lh.with_T(len(pick))
+    xs = np.ascontiguousarray(xh[pick])
+    lg, ids, w = oracle_routing(orc, sub, xs)
+    diff = check_routing(orc, sub, xs, gids[pick], lg, ids, "mxfp4-prefill-4096")
+    ref = orc.forward_with_routing(sub, xs, ids, w)
+    keep = [i for i in range(len(pick)) if i not in diff]
+    check_out(sub, y[pick][keep], ref[keep], "mxfp4-prefill-4096 sampled")
+    assert np.all(np.isfinite(y))
 
 
 def test_qwen_prefill_full_size_sampled(orc, B):
