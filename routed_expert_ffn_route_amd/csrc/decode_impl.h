@@ -827,20 +827,25 @@ int pick_gn(const GN (&list)[N], int nchunks, bool first_fit = false) {
 }
 
 // Down config: among entries leaving at most a quarter of their chunk slots idle, the one
-// with the fewest output rows on the busiest CU (ties: list order); else the fewest idle.
-int pick_down(int nchunks, int H, int ncu) {
-  int best = -1, score = 1 << 30;
+// whose busiest block has the fewest rounds of work items over its 16 waves (a wave keeps
+// two items in flight, so rounds, not rows, set the latency chain), counting D distinct
+// experts' and the shared expert's items; ties go to more chunks per lane (more bytes in
+// flight), then list order.  Else the fewest idle slots.
+int pick_down(int nch, int nchs, int H, int D, int ncu) {
+  int best = -1, score = 1 << 30, bnch = 0;
   for (int i = 0; i < kNDN; ++i) {
     const int cap = kDN[i].G * kDN[i].NCH;
-    if (cap < nchunks || 4 * (cap - nchunks) > cap) continue;
-    const int rb = kWave / kDN[i].G, nrg = (H + rb - 1) / rb;
-    const int sc = ((nrg + ncu - 1) / ncu) * rb;
-    if (sc < score) {
+    if (cap < nch || 4 * (cap - nch) > cap) continue;
+    const int rb = kWave / kDN[i].G, nrg = (H + rb - 1) / rb, nrgb = (nrg + ncu - 1) / ncu;
+    const int items = nrgb * (((nch + cap - 1) / cap) * D + (nchs + cap - 1) / cap);
+    const int sc = (items + 15) / 16;
+    if (sc < score || (sc == score && kDN[i].NCH > bnch)) {
       best = i;
       score = sc;
+      bnch = kDN[i].NCH;
     }
   }
-  return best >= 0 ? best : pick_gn(kDN, nchunks);
+  return best >= 0 ? best : pick_gn(kDN, nch);
 }
 
 template <int XT, int WT, int SWT, int TM, const GN* L, bool XL, bool SEL1>
@@ -915,7 +920,7 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   if (err != hipSuccess) return MOE_EHIP;
 
   // down: at most one block per CU, each over an even share of the row groups
-  const int g3 = pick_down(A.I / dn_epc(WT), A.H, dv.ncu);
+  const int g3 = pick_down(A.I / dn_epc(WT), A.Is / dn_epc(SWT), A.H, D, dv.ncu);
   const int rb3 = kWave / kDN[g3].G;
   int nrg = (A.H + rb3 - 1) / rb3;
   int nrgb = (nrg + dv.ncu - 1) / dv.ncu;
