@@ -34,6 +34,7 @@ constexpr int kPfBM = kPfTileRows;  // rows per tile
 constexpr int kPfBN = 256;     // B rows per block (gate/up: 128 activation columns x 2)
 constexpr int kPfBK = 32;      // reduction step per LDS stage
 constexpr int kPfNS = 3;       // LDS ring depth (two 256-thread blocks per CU)
+constexpr int kPfNSG = 2;      // bf16 down GEMM: two stages, three blocks per CU (short K)
 
 // The router GEMM splits K over this many blocks per output tile when the tiles alone would
 // leave CUs idle (about 512 blocks wanted, at least four 32-deep K-steps per split); the
@@ -219,8 +220,8 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 template <int MODE, int BM, int NS, int WT>
-__global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks,
-                                                                     int part) {
+__global__ __launch_bounds__(2 * BM, BM == 128 ? (NS == 2 ? 3 : 2) : 1)
+void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
   constexpr bool F4 = WT == MOE_MXFP4;
   constexpr int kStageA = BM * kPfBK * 2 / 16;                    // 16-byte units per stage
   constexpr int kStage = kStageA + (F4 ? kPfBN : kPfBN * kPfBK * 2 / 16);
@@ -451,47 +452,56 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void pf_gemm(Args A, PfL
     }
   } else {
     // The bf16 tile goes through LDS (the operand ring is free now), so that the global
-    // stores are whole 16-byte row pieces instead of one 2-byte element per lane.
+    // stores are whole 16-byte row pieces instead of one 2-byte element per lane; when the
+    // ring is smaller than the tile, the two 64-row halves (wm = 0, 1) go one after the other.
     constexpr int CW = MODE == 0 ? kPfBN / 2 : kPfBN;  // output columns of the tile
     constexpr int LDW = CW + 8;                          // padded LDS row (bf16)
-    static_assert(F4 || BM * LDW * 2 <= NS * kStage * 16, "the output tile fits in the ring");
+    constexpr int kHalves = (F4 || BM * LDW * 2 <= NS * kStage * 16) ? 1 : 2;
+    static_assert(F4 || (BM / kHalves) * LDW * 2 <= NS * kStage * 16, "the output rows fit in the ring");
+    constexpr int HR = BM / kHalves;  // tile rows per pass
     uint16_t* ct = (uint16_t*)smem;
-    __syncthreads();  // every wave is done with the ring
     // A lane holds one column of rows R and R + 1 (r even, r + 1); lane pairs swap one value
     // so that the even lane stores (R, c..c+1) and the odd lane (R + 1, c-1..c) as one dword.
     const bool odd = lane & 1;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int hp = 0; hp < kHalves; ++hp) {
+      __syncthreads();  // every wave is done with the ring (or with the previous pass)
+      if (kHalves == 1 || wm == hp) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const int row0 = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
-        const int row = row0 + (odd ? 1 : 0);
-        uint32_t* crow = (uint32_t*)(ct + row * LDW) + ((lane & 31) >> 1);
-        if constexpr (MODE == 0) {
+        for (int m = 0; m < 2; ++m) {
 #pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            const float a = silu_fast(acc[m][pr][r]) * acc[m][2 + pr][r];
-            const float b = silu_fast(acc[m][pr][r + 1]) * acc[m][2 + pr][r + 1];
-            crow[(wn * 64 + pr * 32) / 2] = pair_pack(a, b, odd);
+          for (int r = 0; r < 16; r += 2) {
+            const int row0 = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+            const int row = row0 + (odd ? 1 : 0);
+            uint32_t* crow = (uint32_t*)(ct + (row - hp * HR) * LDW) + ((lane & 31) >> 1);
+            if constexpr (MODE == 0) {
+#pragma unroll
+              for (int pr = 0; pr < 2; ++pr) {
+                const float a = silu_fast(acc[m][pr][r]) * acc[m][2 + pr][r];
+                const float b = silu_fast(acc[m][pr][r + 1]) * acc[m][2 + pr][r + 1];
+                crow[(wn * 64 + pr * 32) / 2] = pair_pack(a, b, odd);
+              }
+            } else {
+              const float wa = row0 < nrows ? s_wt[row0] : 0.f, wb = row0 + 1 < nrows ? s_wt[row0 + 1] : 0.f;
+#pragma unroll
+              for (int n = 0; n < 4; ++n)
+                crow[(wn * 128 + n * 32) / 2] = pair_pack(wa * acc[m][n][r], wb * acc[m][n][r + 1], odd);
+            }
           }
-        } else {
-          const float wa = row0 < nrows ? s_wt[row0] : 0.f, wb = row0 + 1 < nrows ? s_wt[row0 + 1] : 0.f;
-#pragma unroll
-          for (int n = 0; n < 4; ++n)
-            crow[(wn * 128 + n * 32) / 2] = pair_pack(wa * acc[m][n][r], wb * acc[m][n][r + 1], odd);
         }
       }
-    }
-    __syncthreads();
-    constexpr int UPR = CW / 8;  // 16-byte units per tile row
-    for (int u = tid; u < nrows * UPR; u += 2 * BM) {
-      const int row = u / UPR, cu = u - row * UPR, col = n0 + cu * 8;
-      if (col >= N) continue;
-      const uint4 v = *(const uint4*)&ct[row * LDW + cu * 8];
-      if constexpr (MODE == 0)
-        *(uint4*)&L.act[(size_t)(pos0 + row) * Imax + col] = v;
-      else
-        *(uint4*)&L.out[(size_t)s_slot[row] * A.H + col] = v;
+      __syncthreads();
+      constexpr int UPR = CW / 8;  // 16-byte units per tile row
+      const int prow = min(HR, nrows - hp * HR);
+      for (int u = tid; u < prow * UPR; u += 2 * BM) {
+        const int rr = u / UPR, cu = u - rr * UPR, col = n0 + cu * 8, row = hp * HR + rr;
+        if (col >= N) continue;
+        const uint4 v = *(const uint4*)&ct[rr * LDW + cu * 8];
+        if constexpr (MODE == 0)
+          *(uint4*)&L.act[(size_t)(pos0 + row) * Imax + col] = v;
+        else
+          *(uint4*)&L.out[(size_t)s_slot[row] * A.H + col] = v;
+      }
     }
   }
 }
@@ -620,10 +630,10 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
     const int nbt = (A.H + kPfBN - 1) / kPfBN;
     hook.pre("pf_down", st);
     if (!f4) {
-      rc = run((const void*)pf_gemm<1, kPfBM, kPfNS, MOE_BF16>, cap * nbt, nbt, 0, 0);
+      rc = run((const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16>, cap * nbt, nbt, 0, 0);
     } else {
       rc = run((const void*)pf_gemm<1, kPfBM, kPfNS, MOE_MXFP4>, cap * nbt, nbt, 1, f4_lds(1, A.I));
-      if (!rc && shtiles) rc = run((const void*)pf_gemm<1, kPfBM, kPfNS, MOE_BF16>, shtiles * nbt, nbt, 2, 0);
+      if (!rc && shtiles) rc = run((const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16>, shtiles * nbt, nbt, 2, 0);
     }
     hook.post(st);
     if (rc) return rc;
