@@ -22,6 +22,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -314,11 +315,14 @@ constexpr int kWaves = kThreads / kWave;
 
 // Router logits: block e computes logits[t][e] = Wr[e] . x[t] (+ bias) for every token.  Its
 // four waves take contiguous quarters of H (up to four 16-byte chunks per lane in flight per
-// pass) and meet in LDS, where wave 0 adds the four partial sums in a fixed order.  One block
-// per expert spreads the fp32 router rows over the whole chip.
-constexpr int kRouterChunks = 4;
+// pass, fewer for more tokens) and meet in LDS, where wave 0 adds the four partial sums in a
+// fixed order.  One block per expert spreads the fp32 router rows over the whole chip.  The
+// x chunks of a pass are loaded into registers before any is used (loads consumed as they
+// are issued would wait one L2 round trip each).
 template <int XT, int TM>
 __global__ __launch_bounds__(kThreads) void dec_router(Args A) {
+  constexpr int RC = TM <= 4 ? 4 : TM <= 8 ? 2 : 1;  // 16-byte weight chunks per lane per pass
+  typedef typename std::conditional<XT == MOE_F32, float4, uint2>::type XV;
   __shared__ float s_p[kWaves][TM];
   const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int e = blockIdx.x;
@@ -339,12 +343,13 @@ __global__ __launch_bounds__(kThreads) void dec_router(Args A) {
   float acc[TM];
 #pragma unroll
   for (int t = 0; t < TM; ++t) acc[t] = 0.f;
-  for (int c0 = cb; c0 < ce; c0 += kWave * kRouterChunks) {
-    float4 w[kRouterChunks];
-    int cc[kRouterChunks];
-    float okf[kRouterChunks];  // chunks past the quarter's end load chunk 0 and count 0 times
+  for (int c0 = cb; c0 < ce; c0 += kWave * RC) {
+    float4 w[RC];
+    XV xv[RC][TM];
+    int cc[RC];
+    float okf[RC];  // chunks past the quarter's end load chunk 0 and count 0 times
 #pragma unroll
-    for (int m = 0; m < kRouterChunks; ++m) {
+    for (int m = 0; m < RC; ++m) {
       const int c = c0 + lane + kWave * m;
       const bool ok = c < ce;
       cc[m] = ok ? c : 0;
@@ -352,19 +357,23 @@ __global__ __launch_bounds__(kThreads) void dec_router(Args A) {
       w[m] = ldf4(wr + (size_t)cc[m] * 4);
     }
 #pragma unroll
-    for (int m = 0; m < kRouterChunks; ++m) {
+    for (int m = 0; m < RC; ++m) {
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
-        // no branch around the x loads, so that they issue together with the weight loads;
-        // rows past T read row 0 and are never stored
+        // no branch around the x loads; rows past T read row 0 and are never stored
         const int tt = t < A.T ? t : 0;
+        xv[m][t] = *(const XV*)(xb + tt * xstride + (size_t)cc[m] * sizeof(XV));
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < RC; ++m) {
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
         float x0, x1, x2, x3;
         if constexpr (XT == MOE_F32) {
-          const float4 xv = *(const float4*)(xb + tt * xstride + (size_t)cc[m] * 16);
-          x0 = xv.x; x1 = xv.y; x2 = xv.z; x3 = xv.w;
+          x0 = xv[m][t].x; x1 = xv[m][t].y; x2 = xv[m][t].z; x3 = xv[m][t].w;
         } else {
-          const uint2 xv = ldg8(xb + tt * xstride + (size_t)cc[m] * 8);
-          x0 = bf16lo(xv.x); x1 = bf16hi(xv.x); x2 = bf16lo(xv.y); x3 = bf16hi(xv.y);
+          x0 = bf16lo(xv[m][t].x); x1 = bf16hi(xv[m][t].x); x2 = bf16lo(xv[m][t].y); x3 = bf16hi(xv[m][t].y);
         }
         float d = w[m].x * x0;
         d = fmaf(w[m].y, x1, d);
@@ -848,6 +857,22 @@ int pick_down(int nch, int nchs, int H, int D, int ncu) {
   return best >= 0 ? best : pick_gn(kDN, nch);
 }
 
+// The router's token tile is T itself up to 8 (its x loads are not masked per token), else 16.
+template <int XT>
+void* router_fn(int T) {
+  switch (T) {
+    case 1: return (void*)dec_router<XT, 1>;
+    case 2: return (void*)dec_router<XT, 2>;
+    case 3: return (void*)dec_router<XT, 3>;
+    case 4: return (void*)dec_router<XT, 4>;
+    case 5: return (void*)dec_router<XT, 5>;
+    case 6: return (void*)dec_router<XT, 6>;
+    case 7: return (void*)dec_router<XT, 7>;
+    case 8: return (void*)dec_router<XT, 8>;
+    default: return (void*)dec_router<XT, 16>;
+  }
+}
+
 template <int XT, int WT, int SWT, int TM, const GN* L, bool XL, bool SEL1>
 void* gateup_fn(int gi) {
   switch (gi) {
@@ -884,7 +909,7 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   const int S = A.T * A.k, D = S < A.E ? S : A.E;
   void* args1[] = {&A};
   hook.pre("dec_router", st);
-  hipError_t err = hipLaunchKernel((void*)dec_router<XT, TM>, dim3(A.E), dim3(kThreads), args1, 0, st);
+  hipError_t err = hipLaunchKernel(router_fn<XT>(A.T), dim3(A.E), dim3(kThreads), args1, 0, st);
   hook.post(st);
   if (err != hipSuccess) return MOE_EHIP;
   if (route_only) return MOE_OK;
