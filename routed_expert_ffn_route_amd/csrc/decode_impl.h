@@ -197,6 +197,9 @@ __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* u
         bu[m] = usrow[cc[m]];
       }
     }
+    // keep every weight load of the slice ahead of the arithmetic: left to itself the
+    // scheduler reuses registers and waits for each chunk before loading the next
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (XL) {
       if (c0 == 0) {  // the rows of the tokens in `mask` only
         x_rows_store(xr, threadIdx.x, xn, rw, mask, xs);
@@ -914,9 +917,9 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   if (err != hipSuccess) return MOE_EHIP;
   if (route_only) return MOE_OK;
 
-  // x goes through LDS where several tokens meet each weight chunk
+  // x goes through LDS (its loads issued ahead of the weights, read back at LDS latency)
   const size_t xbytes = (size_t)A.T * A.H * (XT == MOE_F32 ? 4 : 2);
-  const bool xl = TM > 1 && xbytes <= kMaxLdsX;
+  const bool xl = xbytes <= kMaxLdsX;
   // shared expert gate/up: one row per wave, in the selection kernel (T > 1) or beside the
   // routed rows of the gate/up kernel (T = 1)
   const int sh_waves = TM == 1 ? kWaves : TM;
@@ -935,7 +938,8 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   const int rb2 = kWaves * (kWave / GUL[g2].G);
   int tiles = (A.I + rb2 - 1) / rb2;
   int sh_blocks = TM == 1 ? nsh : 0;
-  void* f2 = TM == 1 ? gateup_fn<XT, WT, SWT, TM, GUL, false, true>(g2)
+  void* f2 = TM == 1 ? (xl ? gateup_fn<XT, WT, SWT, TM, GUL, true, true>(g2)
+                           : gateup_fn<XT, WT, SWT, TM, GUL, false, true>(g2))
              : xl    ? gateup_fn<XT, WT, SWT, TM, GUL, true, false>(g2)
                      : gateup_fn<XT, WT, SWT, TM, GUL, false, false>(g2);
   void* args2[] = {&A, &tiles, &sh_blocks};
