@@ -573,7 +573,7 @@ int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook) {
     pf_split_router<<<256, 256, 0, st>>>(A, L.planes);
     const int nbt = ((A.E + 63) / 64) * L.ks, tiles = (A.T + kPfBM - 1) / kPfBM;
     const int nblocks = tiles * nbt;
-    pf_gemm<2, kPfBM, kPfNS, MOE_BF16><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks, 0);
+    pf_gemm<2, kPfBM, kPfNSG, MOE_BF16><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks, 0);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   }
