@@ -62,6 +62,9 @@ def test_strerror_covers_codes(lib):
     (dict(E=2048), B.MOE_EUNSUPPORTED), (dict(k=17, E=64), B.MOE_EUNSUPPORTED),
     (dict(act_dtype=0), B.MOE_EUNSUPPORTED), (dict(out_dtype=2), B.MOE_EUNSUPPORTED),
     (dict(expert_dtype=7), B.MOE_EUNSUPPORTED), (dict(shared_dtype=2), B.MOE_EUNSUPPORTED),
+    # MXFP4 on the grouped-GEMM path: a tile's scale rows must fit in LDS (H, I <= 8192)
+    (dict(T=64, expert_dtype=2, H=8224), B.MOE_EUNSUPPORTED),
+    (dict(T=64, expert_dtype=2, I=8192 + 32), B.MOE_EUNSUPPORTED),
 ])
 def test_shape_validation(lib, kw, code):
     rc, _ = _ws(_shape(**kw))
@@ -73,6 +76,8 @@ def test_workspace_sizes_and_paths(lib):
     for kw, path in [(dict(), "decode.bf16"), (dict(T=4, H=2560, E=512, I=768, I_shared=768), "decode.bf16"),
                      (dict(expert_dtype=2, out_dtype=0), "decode.mxfp4"), (dict(T=16), "decode.bf16"),
                      (dict(T=17), "prefill.bf16"), (dict(T=4096), "prefill.bf16"),
+                     (dict(T=4096, H=2560, E=512, I=768, I_shared=768, expert_dtype=2, out_dtype=0),
+                      "prefill.mxfp4"), (dict(T=64, expert_dtype=2, H=8192), "prefill.mxfp4"),
                      (dict(T=4, H=256, E=16, k=2, I=128, I_shared=128, act_dtype=0, expert_dtype=0,
                            shared_dtype=0, out_dtype=0), "decode.f32")]:
         s = _shape(**kw)
