@@ -235,12 +235,21 @@ def test_route_end_to_end(orc, B, T, H, E, k, bias):
     dict(T=2, H=1024, E=1, k=1, I=224, I_shared=32),           # one expert
     dict(T=3, H=256, E=1024, k=16, I=32, I_shared=32),         # max E and k
     dict(T=4, H=4608, E=16, k=2, I=64, I_shared=64),           # row longer than one slice
+    dict(T=16, H=4096, E=32, k=4, I=128, I_shared=64),         # x (128 KiB) too large for LDS
+    dict(T=7, H=5120, E=24, k=3, I=96, I_shared=32),           # token tile 8, x from global
 ])
 def test_decode_edge_shapes_bf16(orc, B, kw):
     say(f"[decode-edge] {kw}")
     Lh, xh = synth.make_layer(**kw, seed=3)
     Ld, xd = synth.to_device(Lh, xh)
     full_check(orc, B, Lh, xh, Ld, xd, f"edge {kw}")
+
+
+def test_decode_fp32_single_token(orc, B):
+    say("[decode-f32-T1]")
+    Lh, xh = synth.make_layer(1, 512, 32, 4, 128, 96, "f32", "f32", "f32", "f32", seed=6)
+    Ld, xd = synth.to_device(Lh, xh)
+    full_check(orc, B, Lh, xh, Ld, xd, "f32 T=1")
 
 
 def test_decode_fp32_out_from_bf16(orc, B):
@@ -300,7 +309,8 @@ def test_ling_mxfp4(orc, B, T, d):
 
 
 def test_mxfp4_small_shapes(orc, B):
-    for kw in (dict(T=1, H=256, E=8, k=2, I=64, I_shared=64), dict(T=6, H=2048, E=16, k=4, I=512, I_shared=96)):
+    for kw in (dict(T=1, H=256, E=8, k=2, I=64, I_shared=64), dict(T=6, H=2048, E=16, k=4, I=512, I_shared=96),
+               dict(T=16, H=2560, E=32, k=4, I=256, I_shared=64)):  # the last: x from global
         say(f"[mxfp4-small] {kw}")
         Lh, xh = synth.make_layer(**kw, act="bf16", expert="mxfp4", shared="bf16", out="f32", seed=5)
         Ld, xd = synth.to_device(Lh, xh)
