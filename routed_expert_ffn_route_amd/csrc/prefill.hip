@@ -521,7 +521,11 @@ __global__ __launch_bounds__(256) void pf_select(Args A, const float* rpart, int
   }
   int* ids = A.ids + (size_t)t * A.k;
   float* w = A.cw + (size_t)t * A.k;
-  select_token(src + (size_t)t * A.E, A.E, A.k, lane, ids, w);
+  __shared__ unsigned s_hist[4][512];
+  if (A.o_ids)  // routing outputs: listed by descending logit
+    select_token(src + (size_t)t * A.E, A.E, A.k, lane, ids, w);
+  else  // the forward pass only needs the set (radix select, fewer instructions)
+    select_set(src + (size_t)t * A.E, A.E, A.k, lane, s_hist[threadIdx.x >> 6], ids, w);
   if (A.o_logits)
     for (int e = lane; e < A.E; e += 64) A.o_logits[(size_t)t * A.E + e] = src[(size_t)t * A.E + e];
   if (A.o_ids && lane < A.k) {  // each lane re-reads only what it wrote itself
