@@ -199,12 +199,16 @@ __device__ __forceinline__ i32x4_t buf_rsrc(const void* base, size_t bytes) {
 
 // 16 bytes per lane from buffer offset voff into LDS at lds_off + 16 * lane.  Written as
 // inline assembly so that the compiler does not treat the pending write to LDS as a reason to
-// wait for every outstanding load before each LDS read: the waits are placed by hand.
+// wait for every outstanding load before each LDS read: the waits are placed by hand.  M0
+// (the LDS base the load reads when it issues) is saved and put back around it.
 __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(lds_off)
-               : "memory", "m0");
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(voff), "s"(rsrc), "s"(lds_off)
+      : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_t*)p;
