@@ -37,8 +37,11 @@
  *   y        [T][H]          out_dtype
  *
  * Error behaviour: every entry point validates all arguments before it
- * enqueues anything; on a negative return nothing was launched and no output
- * was written.  NaN/Inf inputs are not checked; they propagate.
+ * enqueues anything, so MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EALIGN and
+ * MOE_EWORKSPACE mean that nothing was launched and no output was written.
+ * MOE_EHIP means a kernel launch failed; kernels of the same call enqueued
+ * before it may still run, so the outputs and the workspace are then
+ * undefined.  NaN/Inf inputs are not checked; they propagate.
  */
 #ifndef LIBMOE_MOE_H
 #define LIBMOE_MOE_H
@@ -54,7 +57,8 @@ extern "C" {
 #define MOE_OK 0
 #define MOE_EINVAL (-1)        /* null required pointer, bad size, k > E ...   */
 #define MOE_EUNSUPPORTED (-2)  /* dtype combination or shape outside limits    */
-#define MOE_EALIGN (-3)        /* a pointer is not 16-byte aligned             */
+#define MOE_EALIGN (-3)        /* a pointer is not 16-byte aligned (MXFP4 scale
+                                  arrays included)                              */
 #define MOE_EWORKSPACE (-4)    /* workspace null or smaller than required      */
 #define MOE_EHIP (-5)          /* a HIP runtime call or kernel launch failed   */
 
@@ -105,7 +109,11 @@ typedef struct {          /* outputs of moe_route; ids and w required         */
 } moe_route_out_t;
 
 /*
- * Workspace bytes that moe_route / moe_forward need for this shape.  The caller
+ * Workspace bytes that moe_route / moe_forward need for this shape: the router logits, the
+ * per-token selection, the token-to-expert plan and the intermediate activations of the
+ * layer ("Optimizing on-device inference for Apple Silicon", sections "Keep expert routing
+ * on the GPU" and "Reduce intermediate and state traffic": routing stays on the device and
+ * the intermediates the fused steps hand over are the only extra traffic).  The caller
  * allocates that many bytes of device memory (16-byte aligned; hipMalloc's 256-byte
  * alignment is fine) and passes it to every call.  Its contents need no initialisation
  * and carry nothing from one call to the next.  One workspace must not be used by two
@@ -134,14 +142,31 @@ int moe_route(const moe_shape_t *shape, const void *x, const moe_weights_t *w,
 
 /*
  * The whole layer: y = routed experts combined with their weights + shared
- * expert, for all T tokens.  No host synchronisation, no allocation; the
- * launch configuration depends on the shape only, so the call can be
- * captured into a HIP graph.  y must not alias x, the weights or ws.
+ * expert, for all T tokens ("Optimizing on-device inference for Apple
+ * Silicon", sections "Qwen creates three distinct workload shapes" and
+ * "Reduce intermediate and state traffic"; the formulas at the top of this
+ * file).  No host synchronisation, no allocation; the launch configuration
+ * depends on the shape only, so the call can be captured into a HIP graph.
+ * y must not alias x, the weights or ws.
  *   x [T][H] act_dtype, y [T][H] out_dtype, ws/ws_bytes as above,
  *   stream hipStream_t (NULL = default stream).
  */
 int moe_forward(const moe_shape_t *shape, const void *x, const moe_weights_t *w,
                 void *y, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Where moe_forward leaves the routing it used, as byte offsets into its
+ * workspace: the biased router logits [T][E] fp32 at *logits_off, each token's
+ * k experts in ascending expert id [T][k] int32 at *ids_off, and their
+ * combine weights [T][k] fp32 (same order) at *w_off.  Valid once the
+ * stream has run the moe_forward call and until the workspace is used again;
+ * for inspection and tests (the selection the expert kernels consumed, checked
+ * against an independent implementation, "Optimizing on-device inference for
+ * Apple Silicon", section "Keep expert routing on the GPU").
+ * Returns MOE_OK, MOE_EINVAL (null pointer) or a shape-validation error.
+ */
+int moe_workspace_routing(const moe_shape_t *shape, size_t *logits_off,
+                          size_t *ids_off, size_t *w_off);
 
 /*
  * Name of the kernel path moe_forward takes for this shape, e.g.
@@ -152,7 +177,8 @@ int moe_forward(const moe_shape_t *shape, const void *x, const moe_weights_t *w,
  */
 const char *moe_path_name(const moe_shape_t *shape);
 
-/* Static text for a return code. */
+/* Static text for a return code (the codes above; "unknown error code" for
+ * any other value).  Needs no device. */
 const char *moe_strerror(int code);
 
 /*

@@ -71,6 +71,7 @@ def lib():
         for name, args in {
             "orc_logits": [P, P, P, P],
             "orc_select": [P, ctypes.c_int, ctypes.c_int, P, P],
+            "orc_set_weights": [P, ctypes.c_int, ctypes.c_int, P, P],
             "orc_plan": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P],
             "orc_forward_with_routing": [P, P, P, P, P, P],
             "orc_forward": [P, P, P, P, P, P, P],
@@ -146,6 +147,35 @@ def select(logit_row: np.ndarray, k: int):
     if rc:
         raise ValueError(f"orc_select failed ({rc})")
     return ids, w
+
+
+def set_weights(logit_row: np.ndarray, ids) -> np.ndarray:
+    """Combine weights of a given expert set: softmax over all E renormalised over the set."""
+    lr = np.ascontiguousarray(logit_row, dtype=np.float32)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    w = np.empty(ids.size, np.float64)
+    rc = lib().orc_set_weights(_ptr(lr), lr.size, ids.size, _ptr(ids), _ptr(w))
+    if rc:
+        raise ValueError(f"orc_set_weights failed ({rc})")
+    return w
+
+
+def near_tie_selections(logit_row: np.ndarray, k: int, gap: float = 1e-5):
+    """Every selection a token admits when logits within `gap` of its k-th largest logit
+    count as tied: the experts strictly above that band, plus any choice of the rest from the
+    band.  Returns a list of (ids in descending logit order, weights).  One selection when no
+    logit outside the oracle's own choice lies in the band."""
+    import itertools
+    lr = np.ascontiguousarray(logit_row, dtype=np.float32)
+    ids, _ = select(lr, k)
+    kth = float(lr[ids[-1]])
+    band = [e for e in range(lr.size) if abs(float(lr[e]) - kth) < gap]
+    above = [int(e) for e in ids if abs(float(lr[e]) - kth) >= gap]
+    out = []
+    for extra in itertools.combinations(band, k - len(above)):
+        s = above + sorted(extra, key=lambda e: (-float(lr[e]), e))
+        out.append((np.array(s, np.int32), set_weights(lr, s)))
+    return out
 
 
 def select_all(logits_te: np.ndarray, k: int):

@@ -38,6 +38,17 @@ double orc_e8m0_to_double(uint8_t bits) {
   return ldexp(1.0, (int)bits - 127);
 }
 
+/* The 16 e2m1 values and the 256 e8m0 values, filled once when the library is
+ * loaded by calling the two decoders above: orc_weight reads an MXFP4 element
+ * from these tables (the same values, without a libm call per element). */
+static double e2m1_table[16];
+static double e8m0_table[256];
+
+__attribute__((constructor)) static void fill_mx_tables(void) {
+  for (int c = 0; c < 16; ++c) e2m1_table[c] = orc_e2m1_to_double((uint8_t)c);
+  for (int b = 0; b < 256; ++b) e8m0_table[b] = orc_e8m0_to_double((uint8_t)b);
+}
+
 double orc_weight(const void *base, const uint8_t *scales, int dtype,
                   int64_t mat, int64_t rows, int64_t cols, int64_t r,
                   int64_t c) {
@@ -51,7 +62,7 @@ double orc_weight(const void *base, const uint8_t *scales, int dtype,
     uint8_t byte = codes[row * (cols / 2) + c / 2];
     uint8_t nib = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
     uint8_t sc = scales[row * (cols / 32) + c / 32];
-    return orc_e2m1_to_double(nib) * orc_e8m0_to_double(sc);
+    return e2m1_table[nib] * e8m0_table[sc];
   }
 }
 
@@ -106,6 +117,29 @@ int orc_select(const float *lrow, int E, int k, int32_t *ids, double *w) {
   }
   free(taken);
   /* softmax over all E logits, then renormalise the selected ones. */
+  double m = -INFINITY;
+  for (int e = 0; e < E; ++e)
+    if ((double)lrow[e] > m) m = (double)lrow[e];
+  double z = 0.0;
+  for (int e = 0; e < E; ++e) z += exp((double)lrow[e] - m);
+  double sel = 0.0;
+  for (int j = 0; j < k; ++j) {
+    w[j] = exp((double)lrow[ids[j]] - m) / z;
+    sel += w[j];
+  }
+  for (int j = 0; j < k; ++j) w[j] = w[j] / sel;
+  return 0;
+}
+
+int orc_set_weights(const float *lrow, int E, int k, const int32_t *ids,
+                    double *w) {
+  if (E < 1 || k < 1 || k > E) return -1;
+  for (int j = 0; j < k; ++j) {
+    if (ids[j] < 0 || ids[j] >= E) return -1;
+    for (int i = 0; i < j; ++i)
+      if (ids[i] == ids[j]) return -1;
+  }
+  /* p_e = exp(l_e - m) / sum over all E of exp(l - m); then w_j = p_{ids[j]} / sum of the set's p. */
   double m = -INFINITY;
   for (int e = 0; e < E; ++e)
     if ((double)lrow[e] > m) m = (double)lrow[e];

@@ -95,6 +95,13 @@ int orc_logits(const orc_shape *s, const void *x, const orc_weights *w,
 /* R2 + R3 for one token: ids[k] and combine weights w[k] from fp32 logits. */
 int orc_select(const float *logits_row, int E, int k, int32_t *ids, double *w);
 
+/* R3 for a given set of k distinct experts ids[k] (any order): the softmax over
+ * all E logits, renormalised over the set; w[j] belongs to ids[j].  Used to
+ * state the output of every valid selection of a token whose k-th and
+ * (k+1)-th logits are nearly equal. */
+int orc_set_weights(const float *logits_row, int E, int k, const int32_t *ids,
+                    double *w);
+
 /* R7: counts[E], offsets[E+1], sorted_slot[T*k] from ids[T][k]. */
 int orc_plan(const int32_t *ids, int T, int k, int E, int32_t *counts,
              int32_t *offsets, int32_t *sorted_slot);

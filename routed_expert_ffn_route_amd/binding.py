@@ -12,8 +12,8 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
 DTYPES = {"f32": 0, "bf16": 1, "mxfp4": 2}
-EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_path_name", "moe_strerror",
-           "moe_timing_begin", "moe_timing_end")
+EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_workspace_routing", "moe_path_name",
+           "moe_strerror", "moe_timing_begin", "moe_timing_end")
 
 
 class Shape(ctypes.Structure):
@@ -63,6 +63,8 @@ def lib():
                                 ctypes.POINTER(RouteOut), P, ctypes.c_size_t, P]
         L.moe_forward.argtypes = [ctypes.POINTER(Shape), P, ctypes.POINTER(Weights), P, P,
                                   ctypes.c_size_t, P]
+        L.moe_workspace_routing.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t),
+                                            ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
         L.moe_path_name.argtypes = [ctypes.POINTER(Shape)]
         L.moe_path_name.restype = ctypes.c_char_p
         L.moe_strerror.argtypes = [ctypes.c_int]
@@ -70,7 +72,8 @@ def lib():
         L.moe_timing_begin.argtypes = [ctypes.c_int32]
         L.moe_timing_end.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32,
                                      ctypes.POINTER(ctypes.c_int32)]
-        for n in ("moe_workspace_size", "moe_route", "moe_forward", "moe_timing_begin", "moe_timing_end"):
+        for n in ("moe_workspace_size", "moe_route", "moe_forward", "moe_workspace_routing", "moe_timing_begin",
+                  "moe_timing_end"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -133,6 +136,28 @@ def forward(shape: Shape, x, weights: Weights, y, ws, stream=None) -> None:
                            ws.numel() if ws is not None else 0, _stream(stream))
     if rc:
         raise MoeError(rc, "moe_forward")
+
+
+def workspace_routing_offsets(shape: Shape) -> tuple[int, int, int]:
+    """Byte offsets of the logits, the selected ids and their weights that moe_forward
+    leaves in its workspace."""
+    lo, io, wo = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    rc = lib().moe_workspace_routing(ctypes.byref(shape), ctypes.byref(lo), ctypes.byref(io), ctypes.byref(wo))
+    if rc:
+        raise MoeError(rc, "moe_workspace_routing")
+    return lo.value, io.value, wo.value
+
+
+def forward_routing(layer, ws):
+    """(logits [T][E], ids [T][k] ascending per token, weights [T][k]) that the last moe_forward
+    on workspace `ws` used, as views into the workspace tensor."""
+    import torch
+    lo, io, wo = workspace_routing_offsets(shape_of(layer))
+    T, E, k = layer.T, layer.E, layer.k
+    lg = ws[lo:lo + 4 * T * E].view(torch.float32).view(T, E)
+    ids = ws[io:io + 4 * T * k].view(torch.int32).view(T, k)
+    w = ws[wo:wo + 4 * T * k].view(torch.float32).view(T, k)
+    return lg, ids, w
 
 
 def path_name(shape: Shape) -> str:

@@ -13,7 +13,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "decode.hip", "decode_f32.hip", "decode_bf16.hip", "decode_fp4.hip", "prefill.hip"]
+# (source, object, extra defines): decode_inst.hip is compiled once per dtype combination and
+# token tile so that the decode kernels build in parallel
+SOURCES = [("api.hip", "api.o", []), ("route.hip", "route.o", []), ("decode.hip", "decode.o", []),
+           ("prefill.hip", "prefill.o", [])] + [
+    ("decode_inst.hip", f"decode_{n}_t{tm}.o", [f"-DMOE_DEC_NAME={n}", f"-DMOE_DEC_TM={tm}"])
+    for n in ("fp4", "bf16", "f32") for tm in (1, 4, 8, 16)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-Wno-unused-variable",
@@ -22,12 +27,13 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", os.path.join(HERE, "..", "include")]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(unit) -> str:
+    src, objname, defs = unit
+    obj = os.path.join(OBJ, objname)
+    cmd = [HIPCC, *FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for {objname}:\n{r.stdout}\n{r.stderr}")
     warn = [l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
     if warn:
         sys.stderr.write("\n".join(warn) + "\n")
@@ -36,6 +42,9 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
+    for f in os.listdir(OBJ):  # objects of units that no longer exist must not be linked
+        if f.endswith(".o"):
+            os.remove(os.path.join(OBJ, f))
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"

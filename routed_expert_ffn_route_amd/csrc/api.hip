@@ -67,7 +67,7 @@ Layout layout(const moe_shape_t* s) {
     off += up(S * (size_t)s->I * 4);
   } else {
     L.pf = off;
-    off += up(prefill_ws_bytes(s->T, s->H, s->E, s->k, s->I, s->I_shared));
+    off += up(prefill_ws_bytes(s->T, s->H, s->E, s->k, s->I, s->I_shared, s->expert_dtype == MOE_MXFP4));
   }
   L.total = off;
   return L;
@@ -125,6 +125,11 @@ int check_weights(const moe_shape_t* s, const moe_weights_t* w, bool experts) {
   const void* ptrs[] = {w->gate, w->up, w->down, w->sh_gate, w->sh_up, w->sh_down};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_EALIGN;
+  if (s->expert_dtype == MOE_MXFP4) {  // the grouped GEMM stages scale rows with 16-byte loads
+    const void* sc[] = {w->gate_s, w->up_s, w->down_s};
+    for (const void* p : sc)
+      if (!aligned16(p)) return MOE_EALIGN;
+  }
   return MOE_OK;
 }
 
@@ -226,6 +231,17 @@ int moe_forward(const moe_shape_t* shape, const void* x, const moe_weights_t* w,
   time_launch_overhead((hipStream_t)stream);
   if (shape->T <= kDecodeMaxT) return launch_decode(A, (hipStream_t)stream, false, hook());
   return launch_prefill(A, (hipStream_t)stream, hook());
+}
+
+int moe_workspace_routing(const moe_shape_t* shape, size_t* logits_off, size_t* ids_off, size_t* w_off) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!logits_off || !ids_off || !w_off) return MOE_EINVAL;
+  const Layout L = layout(shape);
+  *logits_off = L.logits;
+  *ids_off = L.ids;
+  *w_off = L.cw;
+  return MOE_OK;
 }
 
 const char* moe_path_name(const moe_shape_t* shape) {

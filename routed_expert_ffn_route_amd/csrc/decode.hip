@@ -1,12 +1,24 @@
-// Decode path (T <= 16) dispatch by dtype combination; the kernels are in decode_impl.h,
-// instantiated once per combination in decode_{f32,bf16,fp4}.hip.
+// Decode path (T <= 16) dispatch by dtype combination and token tile; the kernels are in
+// decode_impl.h, instantiated per (combination, tile) by decode_inst.hip.
 #include "kernels.h"
 
 namespace moe {
 
-int launch_decode_f32(Args A, hipStream_t st, bool route_only, const LaunchHook& hook);
-int launch_decode_bf16(Args A, hipStream_t st, bool route_only, const LaunchHook& hook);
-int launch_decode_fp4(Args A, hipStream_t st, bool route_only, const LaunchHook& hook);
+#define MOE_DECL(n)                                                                            \
+  int launch_decode_##n##_t1(Args, hipStream_t, bool, const LaunchHook&);                     \
+  int launch_decode_##n##_t4(Args, hipStream_t, bool, const LaunchHook&);                     \
+  int launch_decode_##n##_t8(Args, hipStream_t, bool, const LaunchHook&);                     \
+  int launch_decode_##n##_t16(Args, hipStream_t, bool, const LaunchHook&);                    \
+  static int launch_decode_##n(Args A, hipStream_t st, bool route_only, const LaunchHook& h) { \
+    if (A.T <= 1) return launch_decode_##n##_t1(A, st, route_only, h);                        \
+    if (A.T <= 4) return launch_decode_##n##_t4(A, st, route_only, h);                        \
+    if (A.T <= 8) return launch_decode_##n##_t8(A, st, route_only, h);                        \
+    return launch_decode_##n##_t16(A, st, route_only, h);                                     \
+  }
+MOE_DECL(f32)
+MOE_DECL(bf16)
+MOE_DECL(fp4)
+#undef MOE_DECL
 
 int launch_decode(Args A, hipStream_t st, bool route_only, const LaunchHook& hook) {
   if (A.act == MOE_F32) return launch_decode_f32(A, st, route_only, hook);

@@ -483,6 +483,11 @@ __global__ __launch_bounds__(kWave * TM) void dec_select(Args A, int nsh) {
     }
   }
   __syncthreads();
+  // the selection itself, for inspection through the workspace (ascending id per token)
+  for (int i = threadIdx.x; i < S; i += nth) {
+    A.ids[i] = s_ids[i];
+    A.cw[i] = s_w[i];
+  }
   // a token's k experts are distinct, so every (distinct expert, token) cell has one writer
   for (int i = threadIdx.x; i < S; i += nth) {
     const int c = s_pos[s_ids[i]] * T + i / k;
@@ -569,6 +574,8 @@ __global__ __launch_bounds__(kThreads) void dec_gateup(Args A, int tiles, int sh
     if (blk == 0 && threadIdx.x < A.k) {
       const int i = threadIdx.x;
       if (i == 0) *P.nd() = A.k;
+      A.ids[i] = s_ids[i];
+      A.cw[i] = s_w[i];
       P.dexp()[i] = s_ids[i];
       P.dmask()[i] = 1u;
       P.dslot()[i] = i;
@@ -661,6 +668,7 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
       for (int m = 0; m < NCH; ++m) {
         const int c = sl * G * NCH + gl + G * m;
         bf.w[m] = DN<SWT>::load(row, c < nchs ? c : 0);
+        if constexpr (WT == MOE_MXFP4) bf.sb[m] = 127u;  // unit scale (never used for shared rows)
       }
       return;
     }
@@ -715,8 +723,10 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
     for (int m = 0; m < NCH; ++m) {
       const int c = sl * G * NCH + gl + G * m;
       cc[m] = c < lim ? c : 0;
-      if constexpr (WT == MOE_MXFP4)  // select, not multiply: a NaN scale must not leak
-        sc[m] = c < lim ? (sh ? 1.f : e8m0_to_f32(bf.sb[m])) : 0.f;
+      if constexpr (WT == MOE_MXFP4) {  // select, not multiply: a NaN scale must not leak
+        const float s = e8m0_to_f32(bf.sb[m]);
+        sc[m] = c < lim ? (sh ? 1.f : s) : 0.f;
+      }
       else
         sc[m] = c < lim ? 1.f : 0.f;
     }
@@ -791,13 +801,16 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
 struct GN { int G, NCH; };
 // gate/up (reduction over H): two rows per wave with 8 chunks per lane for one token;
 // wider groups when several tokens share the x registers
-constexpr GN kGU1[] = {{32, 8}, {64, 4}, {64, 5}, {16, 5}, {16, 4}, {32, 1}, {16, 1}, {64, 1}, {64, 2}, {64, 8}};
-constexpr GN kGUn[] = {{64, 4}, {64, 5}, {16, 5}, {16, 4}, {64, 1}, {64, 2}, {32, 1}, {16, 1}, {32, 8}, {64, 8}};
+// (no two entries of a list have the same capacity G * NCH: the picker takes the first of
+// equal capacities, so a later one would never run)
+constexpr GN kGU1[] = {{32, 8}, {64, 5}, {16, 5}, {16, 4}, {32, 1}, {16, 1}, {64, 2}, {64, 8}};
+constexpr GN kGUn[] = {{64, 4}, {64, 5}, {16, 5}, {16, 4}, {64, 2}, {32, 1}, {16, 1}, {64, 8}};
 // down (reduction over I): activations come from LDS, so several chunks per lane are cheap;
 // the launcher prefers the entry that spreads the output rows most evenly over the CUs
 constexpr GN kDN[] = {{8, 3}, {8, 2}, {16, 4}, {32, 3}, {16, 3}, {8, 4}, {16, 2}, {32, 2},
-                      {16, 1}, {32, 1}, {8, 1}, {64, 8}};
+                      {16, 1}, {32, 1}, {8, 1}, {64, 4}};
 constexpr int kNGU = sizeof(kGU1) / sizeof(kGU1[0]);
+static_assert(kNGU == 8 && sizeof(kGUn) / sizeof(kGUn[0]) == 8, "gateup_fn instantiates 8 entries");
 constexpr int kNDN = sizeof(kDN) / sizeof(kDN[0]);
 
 struct DevInfo { int ncu, max_lds; };
@@ -816,8 +829,8 @@ DevInfo dev_info() {
   return cache[dev];
 }
 
-// First entry with the fewest idle chunk slots; the last entry (64, 8) walks long rows in
-// slices when nothing covers the row.
+// First entry with the fewest idle chunk slots; the last entry walks long rows in slices
+// when nothing covers the row.
 // first_fit: the first entry that leaves at most a quarter of its chunk slots idle.
 template <int N>
 int pick_gn(const GN (&list)[N], int nchunks, bool first_fit = false) {
@@ -880,7 +893,7 @@ template <int XT, int WT, int SWT, int TM, const GN* L, bool XL, bool SEL1>
 void* gateup_fn(int gi) {
   switch (gi) {
 #define C(i) case i: return (void*)dec_gateup<XT, WT, SWT, L[i].G, L[i].NCH, TM, XL, SEL1>;
-    C(0) C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8) C(9)
+    C(0) C(1) C(2) C(3) C(4) C(5) C(6) C(7)
 #undef C
   }
   return nullptr;
@@ -917,9 +930,11 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   if (err != hipSuccess) return MOE_EHIP;
   if (route_only) return MOE_OK;
 
-  // x goes through LDS (its loads issued ahead of the weights, read back at LDS latency)
+  // x goes through LDS (its loads issued ahead of the weights, read back at LDS latency); one
+  // token's row always fits (H <= MOE_MAX_H fp32 values are 64 KiB)
   const size_t xbytes = (size_t)A.T * A.H * (XT == MOE_F32 ? 4 : 2);
-  const bool xl = xbytes <= kMaxLdsX;
+  static_assert((size_t)MOE_MAX_H * 4 <= (size_t)kMaxLdsX, "a single token's x fits in LDS");
+  const bool xl = TM == 1 || xbytes <= kMaxLdsX;
   // shared expert gate/up: one row per wave, in the selection kernel (T > 1) or beside the
   // routed rows of the gate/up kernel (T = 1)
   const int sh_waves = TM == 1 ? kWaves : TM;
@@ -938,10 +953,11 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   const int rb2 = kWaves * (kWave / GUL[g2].G);
   int tiles = (A.I + rb2 - 1) / rb2;
   int sh_blocks = TM == 1 ? nsh : 0;
-  void* f2 = TM == 1 ? (xl ? gateup_fn<XT, WT, SWT, TM, GUL, true, true>(g2)
-                           : gateup_fn<XT, WT, SWT, TM, GUL, false, true>(g2))
-             : xl    ? gateup_fn<XT, WT, SWT, TM, GUL, true, false>(g2)
-                     : gateup_fn<XT, WT, SWT, TM, GUL, false, false>(g2);
+  void* f2;
+  if constexpr (TM == 1)
+    f2 = gateup_fn<XT, WT, SWT, TM, GUL, true, true>(g2);
+  else
+    f2 = xl ? gateup_fn<XT, WT, SWT, TM, GUL, true, false>(g2) : gateup_fn<XT, WT, SWT, TM, GUL, false, false>(g2);
   void* args2[] = {&A, &tiles, &sh_blocks};
   hook.pre("dec_gateup", st);
   err = launch_dyn(f2, dim3(sh_blocks + D * tiles), dim3(kThreads), args2, xl ? xbytes : 0, st);
@@ -968,14 +984,6 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   hook.post(st);
   if (err != hipSuccess) return MOE_EHIP;
   return MOE_OK;
-}
-
-template <int XT, int WT, int SWT>
-int launch_decode_dt(Args A, hipStream_t st, bool route_only, const LaunchHook& hook) {
-  if (A.T <= 1) return launch_decode_t<XT, WT, SWT, 1>(A, st, route_only, hook);
-  if (A.T <= 4) return launch_decode_t<XT, WT, SWT, 4>(A, st, route_only, hook);
-  if (A.T <= 8) return launch_decode_t<XT, WT, SWT, 8>(A, st, route_only, hook);
-  return launch_decode_t<XT, WT, SWT, 16>(A, st, route_only, hook);
 }
 
 }  // namespace

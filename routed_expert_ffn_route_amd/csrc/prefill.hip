@@ -16,6 +16,14 @@
 //           epilogue, one bf16 row per slot.
 //  combine  y[t] = sum_j out[t*k + j] + out_shared[t], a fixed order (deterministic).
 //
+// MXFP4 experts take the precise variant (template flag P) of the same kernels: the gate/up
+// epilogue stores each fp32 activation as two bf16 parts, hi = bf16(a) and lo = bf16(a - hi),
+// the down GEMM multiplies both parts by the same weight fragment (two MFMAs accumulating in
+// fp32, so the activations keep about 16 significant bits instead of 8), and the per-slot rows
+// stay fp32 through the combine.  The MXFP4 layer is held to a relative L2 error of 1e-3
+// against the exactly dequantised layer, which bf16 activations and bf16 slot rows (each
+// rounding costs about 1e-3 on its own) would not meet.
+//
 // All three GEMMs run one kernel, pf_gemm: 128 x 256 block tiles, K-steps of 32 staged in
 // a three-deep LDS ring that the buffer unit fills directly (loads to LDS, no register
 // staging), rows XOR-swizzled so that MFMA fragment reads are free of bank conflicts.
@@ -45,14 +53,15 @@ int pf_router_splits(int T, int H, int E) {
   return std::max(1, std::min(want, most));
 }
 
-size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is) {
+size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is, bool precise) {
   const size_t S = (size_t)T * k, R = S + T;
   const size_t Imax = I > Is ? I : Is;
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
   const int ks = pf_router_splits(T, H, E);
+  const size_t np = precise ? 2 : 1;  // activation parts; slot rows fp32 instead of bf16
   return up(sizeof(int) * (E + 2)) * 2 + up(sizeof(int) * R) +
-         up(sizeof(int) * 4 * (size_t)prefill_tiles_cap(T, E, k)) + up(256) + up(2 * R * Imax) +
-         up(2 * R * (size_t)H) + up(2 * 3 * (size_t)E * H) +
+         up(sizeof(int) * 4 * (size_t)prefill_tiles_cap(T, E, k)) + up(256) + np * up(2 * R * Imax) +
+         up(2 * np * R * (size_t)H) + up(2 * 3 * (size_t)E * H) +
          (ks > 1 ? up(sizeof(float) * (size_t)ks * T * E) : 0) +
          up(sizeof(int) * (size_t)permute_blocks(T, k) * E);
 }
@@ -70,8 +79,10 @@ struct PfLayout {
   int* rows;    // [S+T]
   int* tiles;   // [cap] x {group, first row, rows, 0}
   int* ntiles;  // [1]
-  uint16_t* act;  // [S+T][Imax]
-  uint16_t* out;  // [S+T][H]
+  uint16_t* act;     // [S+T][Imax] bf16 activations (precise: their hi parts)
+  uint16_t* act_lo;  // precise: [S+T][Imax] the lo parts, else null
+  uint16_t* out;     // [S+T][H] bf16 weighted slot rows (precise: null)
+  float* outf;       // precise: [S+T][H] fp32 weighted slot rows, else null
   uint16_t* planes;  // [3][E][H] bf16 parts of the router weights
   float* rpart;      // [ks][T][E] partial router logits (K split ks > 1 ways), else null
   int ks;
@@ -94,10 +105,17 @@ PfLayout pf_layout(const Args& A) {
   b += up(sizeof(int) * 4 * (size_t)prefill_tiles_cap(A.T, A.E, A.k));
   L.ntiles = (int*)b;
   b += up(256);
+  const bool precise = A.wdt == MOE_MXFP4;
   L.act = (uint16_t*)b;
   b += up(2 * R * Imax);
-  L.out = (uint16_t*)b;
-  b += up(2 * R * (size_t)A.H);
+  L.act_lo = nullptr;
+  if (precise) {
+    L.act_lo = (uint16_t*)b;
+    b += up(2 * R * Imax);
+  }
+  L.out = precise ? nullptr : (uint16_t*)b;
+  L.outf = precise ? (float*)b : nullptr;
+  b += up((precise ? 4 : 2) * R * (size_t)A.H);
   L.planes = (uint16_t*)b;
   b += up(2 * 3 * (size_t)A.E * A.H);
   L.ks = pf_router_splits(A.T, A.H, A.E);
@@ -223,16 +241,29 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int MODE, int BM, int NS, int WT>
+// LDS sizes of one pf_gemm instance (16-byte units); the host sizes dynamic LDS from them.
+template <int MODE, int BM, int NS, int WT, bool P>
+struct PfCfg {
+  static constexpr bool F4 = WT == MOE_MXFP4;
+  static constexpr bool AHL = P && MODE == 1;                    // A = activation hi and lo parts
+  static constexpr int kUnitsA = BM * kPfBK * 2 / 16;             // one A part per stage
+  static constexpr int kStageA = kUnitsA * (AHL ? 2 : 1);
+  static constexpr int kStage = kStageA + (F4 ? kPfBN : kPfBN * kPfBK * 2 / 16);
+  static constexpr int kNA = AHL ? 4 : 2;                         // A load instructions per wave per step
+  static constexpr int kNB = F4 ? 1 : 512 / BM;                   // B load instructions per wave per step
+  static constexpr bool kDyn = F4 || P;                           // LDS sized at launch
+  static constexpr size_t ring_bytes = (size_t)NS * kStage * 16;
+};
+
+template <int MODE, int BM, int NS, int WT, bool P>
 __global__ __launch_bounds__(2 * BM, BM == 128 ? (NS == 2 ? 3 : 2) : 1)
 void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
-  constexpr bool F4 = WT == MOE_MXFP4;
-  constexpr int kStageA = BM * kPfBK * 2 / 16;                    // 16-byte units per stage
-  constexpr int kStage = kStageA + (F4 ? kPfBN : kPfBN * kPfBK * 2 / 16);
-  constexpr int kNB = F4 ? 1 : 512 / BM;                          // B load instructions per wave per step
+  typedef PfCfg<MODE, BM, NS, WT, P> C;
+  constexpr bool F4 = C::F4;
+  constexpr int kStageA = C::kStageA, kStage = C::kStage, kNA = C::kNA, kNB = C::kNB;
   extern __shared__ __attribute__((aligned(16))) uint4 smem_dyn[];
-  __shared__ __attribute__((aligned(16))) uint4 smem_st[F4 ? 1 : NS * kStage];
-  uint4* smem = F4 ? smem_dyn : smem_st;
+  __shared__ __attribute__((aligned(16))) uint4 smem_st[C::kDyn ? 1 : NS * kStage];
+  uint4* smem = C::kDyn ? smem_dyn : smem_st;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -272,11 +303,12 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
   const int n0 = MODE == 0 ? nb * (kPfBN / 2) : MODE == 1 ? nb * kPfBN : nb * 64;
   if (n0 >= N) return;
 
-  // ---- per-lane load slots: 2 A and 4 B 16-byte chunks per K-step
-  i32x4_t ra, rb[kNB];
+  // ---- per-lane load slots: 2 A (precise down: 2 hi + 2 lo) and kNB B 16-byte chunks per K-step
+  i32x4_t ra, ra_lo, rb[kNB];
   uint32_t ao[2], bo[kNB];
   if constexpr (MODE == 0) ra = buf_rsrc(A.x, (size_t)A.T * A.H * 2);
   if constexpr (MODE == 1) ra = buf_rsrc(L.act + (size_t)pos0 * Imax, (size_t)nrows * Imax * 2);
+  if constexpr (C::AHL) ra_lo = buf_rsrc(L.act_lo + (size_t)pos0 * Imax, (size_t)nrows * Imax * 2);
   if constexpr (MODE == 2) ra = buf_rsrc((const uint16_t*)A.x + (size_t)ti * BM * A.H, (size_t)nrows * A.H * 2);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -362,6 +394,10 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
     const uint32_t kb = ks * kPfBK * 2u, kbb = F4 ? ks * 16u : kb;
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(ra, ao[j] + kb, lds_addr(stage + (wave * 2 + j) * 64));
+    if constexpr (C::AHL) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) dma16(ra_lo, ao[j] + kb, lds_addr(stage + C::kUnitsA + (wave * 2 + j) * 64));
+    }
 #pragma unroll
     for (int j = 0; j < kNB; ++j) dma16(rb[j], bo[j] + kbb, lds_addr(stage + kStageA + (wave * kNB + j) * 64));
   };
@@ -394,17 +430,20 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
   const int mlive = min(2, max(0, (nrows - wm * 64 + 31) / 32));
   f32x16_t acc[2][4] = {};
   auto step = [&](int s) {
-    wait_vm<(2 + kNB) * (NS - 2)>();  // this wave's loads of step s have landed (later ones in flight)
+    wait_vm<(kNA + kNB) * (NS - 2)>();  // this wave's loads of step s have landed (later ones in flight)
     __syncthreads();          // ... and every other wave's; all are done with step s - 1's stage
     issue(s + NS - 1, smem + ((s + NS - 1) % NS) * kStage);
     const uint4* st = smem + (s % NS) * kStage;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int c = ks * 2 + (lane >> 5);
-      bf16x8_t af[2], bfr[4];
+      bf16x8_t af[2], afl[2], bfr[4];
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < 2; ++m) {
         af[m] = __builtin_bit_cast(bf16x8_t, st[swz_unit(wm * 64 + m * 32 + (lane & 31), c)]);
+        if constexpr (C::AHL)
+          afl[m] = __builtin_bit_cast(bf16x8_t, st[C::kUnitsA + swz_unit(wm * 64 + m * 32 + (lane & 31), c)]);
+      }
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int br = wn * 128 + n * 32 + (lane & 31);
@@ -425,7 +464,10 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
       for (int m = 0; m < 2; ++m) {
         if (m >= mlive) break;  // uniform
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[m][n] = mfma32(af[m], bfr[n], acc[m][n]);
+        for (int n = 0; n < 4; ++n) {
+          acc[m][n] = mfma32(af[m], bfr[n], acc[m][n]);
+          if constexpr (C::AHL) acc[m][n] = mfma32(afl[m], bfr[n], acc[m][n]);
+        }
       }
     }
   };
@@ -454,19 +496,42 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
         }
       }
     }
+  } else if constexpr (MODE == 1 && P) {
+    // precise down: fp32 weighted rows straight from the accumulators; lanes 0-31 and 32-63
+    // of a store hold 32 consecutive columns of two rows, two whole 128-byte pieces
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+        if (row >= nrows) continue;
+        const float wt = s_wt[row];
+        float* orow = L.outf + (size_t)s_slot[row] * A.H;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int col = n0 + wn * 128 + n * 32 + (lane & 31);
+          if (col < N) orow[col] = wt * acc[m][n][r];
+        }
+      }
+    }
   } else {
     // The bf16 tile goes through LDS (the operand ring is free now), so that the global
     // stores are whole 16-byte row pieces instead of one 2-byte element per lane; when the
     // ring is smaller than the tile, the two 64-row halves (wm = 0, 1) go one after the other.
+    // Precise gate/up stores two planes, the activations' bf16 hi parts and then their lo
+    // parts (a - hi, rounded to bf16), one pass each.
     constexpr int CW = MODE == 0 ? kPfBN / 2 : kPfBN;  // output columns of the tile
     constexpr int LDW = CW + 8;                          // padded LDS row (bf16)
-    constexpr int kHalves = (F4 || BM * LDW * 2 <= NS * kStage * 16) ? 1 : 2;
-    static_assert(F4 || (BM / kHalves) * LDW * 2 <= NS * kStage * 16, "the output rows fit in the ring");
+    constexpr int kHalves = (C::kDyn || BM * LDW * 2 <= NS * kStage * 16) ? 1 : 2;
+    static_assert(C::kDyn || (BM / kHalves) * LDW * 2 <= NS * kStage * 16, "the output rows fit in the ring");
     constexpr int HR = BM / kHalves;  // tile rows per pass
+    constexpr int kPlanes = P ? 2 : 1;
     uint16_t* ct = (uint16_t*)smem;
     // A lane holds one column of rows R and R + 1 (r even, r + 1); lane pairs swap one value
     // so that the even lane stores (R, c..c+1) and the odd lane (R + 1, c-1..c) as one dword.
     const bool odd = lane & 1;
+#pragma unroll
+    for (int pl = 0; pl < kPlanes; ++pl) {
 #pragma unroll
     for (int hp = 0; hp < kHalves; ++hp) {
       __syncthreads();  // every wave is done with the ring (or with the previous pass)
@@ -481,8 +546,12 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
             if constexpr (MODE == 0) {
 #pragma unroll
               for (int pr = 0; pr < 2; ++pr) {
-                const float a = silu_fast(acc[m][pr][r]) * acc[m][2 + pr][r];
-                const float b = silu_fast(acc[m][pr][r + 1]) * acc[m][2 + pr][r + 1];
+                float a = silu_fast(acc[m][pr][r]) * acc[m][2 + pr][r];
+                float b = silu_fast(acc[m][pr][r + 1]) * acc[m][2 + pr][r + 1];
+                if (P && pl == 1) {  // the lo parts: what bf16 rounding left out (exact in fp32)
+                  a -= bf16_to_f32(f32_to_bf16(a));
+                  b -= bf16_to_f32(f32_to_bf16(b));
+                }
                 crow[(wn * 64 + pr * 32) / 2] = pair_pack(a, b, odd);
               }
             } else {
@@ -497,15 +566,17 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
       __syncthreads();
       constexpr int UPR = CW / 8;  // 16-byte units per tile row
       const int prow = min(HR, nrows - hp * HR);
+      uint16_t* const dst = MODE == 0 ? (pl == 0 ? L.act : L.act_lo) : L.out;
       for (int u = tid; u < prow * UPR; u += 2 * BM) {
         const int rr = u / UPR, cu = u - rr * UPR, col = n0 + cu * 8, row = hp * HR + rr;
         if (col >= N) continue;
         const uint4 v = *(const uint4*)&ct[rr * LDW + cu * 8];
         if constexpr (MODE == 0)
-          *(uint4*)&L.act[(size_t)(pos0 + row) * Imax + col] = v;
+          *(uint4*)&dst[(size_t)(pos0 + row) * Imax + col] = v;
         else
-          *(uint4*)&L.out[(size_t)s_slot[row] * A.H + col] = v;
+          *(uint4*)&dst[(size_t)s_slot[row] * A.H + col] = v;
       }
+    }
     }
   }
 }
@@ -547,6 +618,13 @@ __global__ __launch_bounds__(256) void pf_combine(Args A, PfLayout L) {
   const int S = A.T * A.k;
   float acc[8] = {};
   auto add = [&](int row) {
+    if (L.outf) {  // precise: fp32 slot rows
+      const float4 a = *(const float4*)&L.outf[(size_t)row * A.H + c];
+      const float4 b = *(const float4*)&L.outf[(size_t)row * A.H + c + 4];
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+      return;
+    }
     const uint4 v = *(const uint4*)&L.out[(size_t)row * A.H + c];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -581,7 +659,7 @@ int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook) {
     pf_split_router<<<256, 256, 0, st>>>(A, L.planes);
     const int nbt = ((A.E + 63) / 64) * L.ks, tiles = (A.T + kPfBM - 1) / kPfBM;
     const int nblocks = tiles * nbt;
-    pf_gemm<2, kPfBM, kPfNSG, MOE_BF16><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks, 0);
+    pf_gemm<2, kPfBM, kPfNSG, MOE_BF16, false><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks, 0);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   }
@@ -592,6 +670,19 @@ int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook) {
   if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }
+
+namespace {
+// Dynamic LDS of a pf_gemm instance for reduction length K: the operand ring plus, for MXFP4,
+// the four waves' scale blocks (after the ring), or the bf16 output tile if that is larger.
+template <int MODE, int NS, int WT, bool P>
+size_t pf_lds(int K) {
+  typedef PfCfg<MODE, kPfBM, NS, WT, P> C;
+  if (!C::kDyn) return 0;
+  const size_t sc = C::F4 ? (size_t)4 * ((64 * (K / 32) + 1023) / 1024) * 1024 : 0;
+  const size_t epi = (MODE == 1 && P) ? 0 : (size_t)kPfBM * ((MODE == 0 ? kPfBN / 2 : kPfBN) + 8) * 2;
+  return std::max(C::ring_bytes + sc, epi);
+}
+}  // namespace
 
 int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   const PfLayout L = pf_layout(A);
@@ -606,14 +697,8 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   const int cap = prefill_tiles_cap(A.T, A.E, A.k);
   const int Imax = A.I > A.Is ? A.I : A.Is;
   const bool f4 = A.wdt == MOE_MXFP4;
-  // MXFP4 experts: the routed groups' tiles run the MXFP4 kernel (dynamic LDS: ring, scale
-  // rows, or the output tile if larger), the shared expert's tiles the bf16 kernel
-  auto f4_lds = [&](int mode, int K) {
-    const size_t ring = (size_t)kPfNS * (kPfBM * kPfBK * 2 + kPfBN * 16);
-    const size_t sc = (size_t)4 * ((64 * (K / 32) + 1023) / 1024) * 1024;  // four waves' scale blocks
-    const size_t epi = (size_t)kPfBM * ((mode == 0 ? kPfBN / 2 : kPfBN) + 8) * 2;
-    return std::max(ring + sc, epi);
-  };
+  // MXFP4 experts: the routed groups' tiles run the MXFP4 kernel, the shared expert's tiles the
+  // bf16 kernel, both in the precise variant (activation hi + lo parts, fp32 slot rows)
   auto run = [&](const void* f, int nblocks, int nbt, int part, size_t lds) -> int {
     if (lds > 65536 && hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return MOE_EHIP;
@@ -626,10 +711,13 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
     const int nbt = (Imax + kPfBN / 2 - 1) / (kPfBN / 2);
     hook.pre("pf_gateup", st);
     if (!f4) {
-      rc = run((const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16>, cap * nbt, nbt, 0, 0);
+      rc = run((const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, false>, cap * nbt, nbt, 0, 0);
     } else {
-      rc = run((const void*)pf_gemm<0, kPfBM, kPfNS, MOE_MXFP4>, cap * nbt, nbt, 1, f4_lds(0, A.H));
-      if (!rc && shtiles) rc = run((const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16>, shtiles * nbt, nbt, 2, 0);
+      rc = run((const void*)pf_gemm<0, kPfBM, kPfNS, MOE_MXFP4, true>, cap * nbt, nbt, 1,
+               pf_lds<0, kPfNS, MOE_MXFP4, true>(A.H));
+      if (!rc && shtiles)
+        rc = run((const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, true>, shtiles * nbt, nbt, 2,
+                 pf_lds<0, kPfNS, MOE_BF16, true>(A.H));
     }
     hook.post(st);
     if (rc) return rc;
@@ -638,10 +726,13 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
     const int nbt = (A.H + kPfBN - 1) / kPfBN;
     hook.pre("pf_down", st);
     if (!f4) {
-      rc = run((const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16>, cap * nbt, nbt, 0, 0);
+      rc = run((const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, false>, cap * nbt, nbt, 0, 0);
     } else {
-      rc = run((const void*)pf_gemm<1, kPfBM, kPfNS, MOE_MXFP4>, cap * nbt, nbt, 1, f4_lds(1, A.I));
-      if (!rc && shtiles) rc = run((const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16>, shtiles * nbt, nbt, 2, 0);
+      rc = run((const void*)pf_gemm<1, kPfBM, kPfNS, MOE_MXFP4, true>, cap * nbt, nbt, 1,
+               pf_lds<1, kPfNS, MOE_MXFP4, true>(A.I));
+      if (!rc && shtiles)
+        rc = run((const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, true>, shtiles * nbt, nbt, 2,
+                 pf_lds<1, kPfNSG, MOE_BF16, true>(A.Is));
     }
     hook.post(st);
     if (rc) return rc;

@@ -10,66 +10,6 @@
 namespace moe {
 
 
-// ------------------------------------------------------------------------------------------
-// Router logits for many tokens: [T][H] x [E][H]^T on fp32 VALU FMAs, 64x64 output tiles,
-// K staged through LDS in steps of 32.  (x bf16 or fp32, router fp32.)
-// ------------------------------------------------------------------------------------------
-template <int XT>
-__global__ __launch_bounds__(256) void router_tiled(Args A) {
-  constexpr int BT = 64, BE = 64, BK = 32;
-  __shared__ float sx[BK][BT + 1];
-  __shared__ float sw[BK][BE + 1];
-  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;  // 16 x 16 threads, 4 x 4 each
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < A.H; k0 += BK) {
-    // 64 rows x 32 k of x and of W: 2048 elements each, 8 per thread
-    for (int i = threadIdx.x; i < BT * BK; i += 256) {
-      const int r = i / BK, kk = i % BK;
-      const int t = t0 + r, e = e0 + r;
-      float xv = 0.f, wv = 0.f;
-      if (t < A.T) {
-        if constexpr (XT == MOE_F32)
-          xv = ((const float*)A.x)[(size_t)t * A.H + k0 + kk];
-        else
-          xv = bf16_to_f32(((const uint16_t*)A.x)[(size_t)t * A.H + k0 + kk]);
-      }
-      if (e < A.E) wv = A.rw[(size_t)e * A.H + k0 + kk];
-      sx[kk][r] = xv;
-      sw[kk][r] = wv;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < BK; ++kk) {
-      float xr[4], wr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xr[i] = sx[kk][ty * 4 + i];
-        wr[i] = sw[kk][tx * 4 + i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xr[i], wr[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= A.T) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e >= A.E) continue;
-      float l = acc[i][j];
-      if (A.rbias) l += A.rbias[(size_t)t * A.bias_stride + e];
-      A.logits[(size_t)t * A.E + e] = l;
-      if (A.o_logits) A.o_logits[(size_t)t * A.E + e] = l;
-    }
-  }
-}
-
 // One wave per token: selection from ws logits (or logits_in), written to the workspace
 // ids/weights and, when given, to the moe_route outputs.
 __global__ __launch_bounds__(256) void select_tokens(Args A) {
@@ -111,76 +51,114 @@ __device__ int wave_scan_lds(int* v, int n, int lane) {
   return __shfl(incl, kWave - 1, kWave);
 }
 
-// Histogram -> exclusive scan -> scatter, in one 1024-thread block.  Groups are the E
-// experts plus, when with_shared, a final group E holding every token (the shared expert)
-// as rows S + t.  Writes counts [G], offsets [G+1], rows [S (+T)], and when tiles != null the
-// block map: for each group, ceil(count / bm) tiles {group, first row, rows, 0} (16 bytes
-// each), their number in tiles_n.  The order inside a group is whatever the LDS atomics produce.
-__global__ __launch_bounds__(1024) void permute(const int* ids, int T, int k, int E, bool with_shared,
-                                                int* counts, int* offsets, int* rows, int* tiles,
-                                                int* tiles_n, int bm) {
-  __shared__ int s_cnt[MOE_MAX_E + 2];
-  __shared__ int s_off[MOE_MAX_E + 2];
-  __shared__ int s_til[MOE_MAX_E + 2];
-  __shared__ int s_total, s_ntiles;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int S = T * k, G = E + (with_shared ? 1 : 0);
-  for (int g = tid; g < G; g += 1024) s_cnt[g] = 0;
-  __syncthreads();
-  for (int s = tid; s < S; s += 1024) atomicAdd(&s_cnt[ids[s]], 1);
-  __syncthreads();
-  if (tid == 0 && with_shared) s_cnt[E] = T;
-  __syncthreads();
-  for (int g = tid; g < G; g += 1024) {
-    s_off[g] = s_cnt[g];
-    s_til[g] = (s_cnt[g] + bm - 1) / bm;
+// Stable placement of the assignments [s0, s1) (at most kPermChunk of them) by a block of
+// kPermThreads threads: slot s goes to cursor[e] + the number of earlier slots of the range
+// routed to the same expert e, so each expert group lists its slots in ascending order (the
+// stable counting sort of the page's histogram / scan / scatter, "Optimizing on-device
+// inference for Apple Silicon", section "Keep expert routing on the GPU").  Wave w takes
+// slots s0 + 128 w ... in two passes of 64 lanes; the lanes of a pass that share an expert
+// are found with one ballot per bit of the expert id, so no LDS atomic decides an order.
+// cursor[E] (LDS) advances by the range's count of each expert.  s_wh: LDS [4][E] ints, zero
+// on entry and on exit.
+constexpr int kPermChunk = 512;
+constexpr int kPermThreads = 256;
+
+__device__ __forceinline__ uint64_t same_expert_lanes(int e, bool valid, int nbits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t ones = __ballot(valid && bit);
+    m &= bit ? ones : ~ones;
   }
+  return valid ? m : 0ull;
+}
+
+__device__ void stable_place(const int* ids, int s0, int s1, int E, int* cursor, int* s_wh, int* rows) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int e[2], rank[2], cnt[2];
+  bool ok[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {  // counts per (wave, expert): one writer per group of lanes
+    const int s = s0 + 128 * w + 64 * p + lane;
+    ok[p] = s < s1;
+    e[p] = ok[p] ? ids[s] : 0;
+    const uint64_t m = same_expert_lanes(e[p], ok[p], nbits);
+    rank[p] = __popcll(m & lt);
+    cnt[p] = __popcll(m);
+    if (ok[p] && rank[p] == 0) s_wh[w * E + e[p]] += cnt[p];
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < E; g += blockDim.x) {  // start of each wave's run of expert g
+    int run = cursor[g];
+#pragma unroll
+    for (int ww = 0; ww < kPermThreads / kWave; ++ww) {
+      const int c = s_wh[ww * E + g];
+      s_wh[ww * E + g] = run;
+      run += c;
+    }
+    cursor[g] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int s = s0 + 128 * w + 64 * p + lane;
+    const int start = ok[p] ? s_wh[w * E + e[p]] : 0;
+    __builtin_amdgcn_wave_barrier();  // every lane has read its start before the leader moves it
+    if (ok[p]) {
+      rows[start + rank[p]] = s;
+      if (rank[p] == 0) s_wh[w * E + e[p]] = start + cnt[p];
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < (kPermThreads / kWave) * E; i += blockDim.x) s_wh[i] = 0;
+  __syncthreads();
+}
+
+// Histogram -> exclusive scan -> stable scatter in one block (the routing outputs of
+// moe_route): counts [E], offsets [E+1], sorted slots [S] (nullable each).
+__global__ __launch_bounds__(kPermThreads) void permute(const int* ids, int T, int k, int E, int* counts,
+                                                       int* offsets, int* rows) {
+  __shared__ int s_cnt[MOE_MAX_E + 1];
+  __shared__ int s_off[MOE_MAX_E + 1];
+  __shared__ int s_wh[(kPermThreads / kWave) * MOE_MAX_E];
+  __shared__ int s_total;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int S = T * k;
+  for (int g = tid; g < E; g += blockDim.x) s_cnt[g] = 0;
+  for (int i = tid; i < (kPermThreads / kWave) * E; i += blockDim.x) s_wh[i] = 0;
+  __syncthreads();
+  for (int s = tid; s < S; s += blockDim.x) atomicAdd(&s_cnt[ids[s]], 1);  // counts: order-free
+  __syncthreads();
+  for (int g = tid; g < E; g += blockDim.x) s_off[g] = s_cnt[g];
   __syncthreads();
   if (tid < kWave) {
-    int tot = wave_scan_lds(s_off, G, lane);
+    const int tot = wave_scan_lds(s_off, E, lane);
     if (lane == 0) s_total = tot;
-  } else if (tid < 2 * kWave && tiles) {
-    int tot = wave_scan_lds(s_til, G, lane);
-    if (lane == 0) s_ntiles = tot;
   }
   __syncthreads();
-  for (int g = tid; g < G; g += 1024) {
+  for (int g = tid; g < E; g += blockDim.x) {
     if (counts) counts[g] = s_cnt[g];
     if (offsets) offsets[g] = s_off[g];
   }
-  if (tid == 0) {
-    if (offsets) offsets[G] = s_total;
-    if (tiles_n) *tiles_n = tiles ? s_ntiles : 0;
-  }
-  if (tiles) {
-    for (int g = tid; g < G; g += 1024) {
-      const int nt = (s_cnt[g] + bm - 1) / bm;
-      for (int i = 0; i < nt; ++i)
-        ((int4*)tiles)[s_til[g] + i] = make_int4(g, s_off[g] + i * bm, min(bm, s_cnt[g] - i * bm), 0);
-    }
-  }
-  __syncthreads();
+  if (tid == 0 && offsets) offsets[E] = s_total;
+  if (!rows) return;  // uniform
   // s_cnt becomes the scatter cursor
-  for (int g = tid; g < G; g += 1024) s_cnt[g] = s_off[g];
+  for (int g = tid; g < E; g += blockDim.x) s_cnt[g] = s_off[g];
   __syncthreads();
-  if (rows) {
-    for (int s = tid; s < S; s += 1024) {
-      const int pos = atomicAdd(&s_cnt[ids[s]], 1);
-      rows[pos] = s;
-    }
-    if (with_shared)
-      for (int t = tid; t < T; t += 1024) rows[s_off[E] + t] = S + t;
-  }
+  for (int s0 = 0; s0 < S; s0 += kPermChunk) stable_place(ids, s0, min(S, s0 + kPermChunk), E, s_cnt, s_wh, rows);
 }
 
 // The same permutation over many blocks, for the forward pass's large T: the assignments are
 // cut into chunks of kPermChunk; (1) each block counts its chunk's experts in LDS and writes
 // its counts per expert, (2) one block adds them up per expert, turns each block's count into
 // its start inside the expert's group (a prefix over blocks), scans the group sizes into
-// offsets and writes the block map, (3) each block scatters its chunk from those starts with
-// LDS cursors.  bcnt: [nblocks][E] ints of workspace.
-constexpr int kPermChunk = 512;
-__global__ __launch_bounds__(256) void permute_count(const int* ids, int S, int E, int* bcnt) {
+// offsets and writes the block map, (3) each block places its chunk stably from those starts.
+// bcnt: [nblocks][E] ints of workspace.
+__global__ __launch_bounds__(kPermThreads) void permute_count(const int* ids, int S, int E, int* bcnt) {
   __shared__ int s_h[MOE_MAX_E];
   for (int g = threadIdx.x; g < E; g += blockDim.x) s_h[g] = 0;
   __syncthreads();
@@ -244,13 +222,15 @@ __global__ __launch_bounds__(1024) void permute_plan(int* bcnt, int nb, int T, i
     for (int t = tid; t < T; t += blockDim.x) rows[s_off[E] + t] = S + t;
 }
 
-__global__ __launch_bounds__(256) void permute_scatter(const int* ids, int S, int E, const int* bcnt,
-                                                       const int* offsets, int* rows) {
+__global__ __launch_bounds__(kPermThreads) void permute_scatter(const int* ids, int S, int E, const int* bcnt,
+                                                                 const int* offsets, int* rows) {
   __shared__ int s_cur[MOE_MAX_E];
+  __shared__ int s_wh[(kPermThreads / kWave) * MOE_MAX_E];
   for (int g = threadIdx.x; g < E; g += blockDim.x) s_cur[g] = offsets[g] + bcnt[(size_t)blockIdx.x * E + g];
+  for (int i = threadIdx.x; i < (kPermThreads / kWave) * E; i += blockDim.x) s_wh[i] = 0;
   __syncthreads();
-  const int s0 = blockIdx.x * kPermChunk, s1 = min(S, s0 + kPermChunk);
-  for (int s = s0 + threadIdx.x; s < s1; s += blockDim.x) rows[atomicAdd(&s_cur[ids[s]], 1)] = s;
+  const int s0 = blockIdx.x * kPermChunk;
+  stable_place(ids, s0, min(S, s0 + kPermChunk), E, s_cur, s_wh, rows);
 }
 
 int permute_blocks(int T, int k) { return (T * k + kPermChunk - 1) / kPermChunk; }
@@ -258,29 +238,21 @@ int permute_blocks(int T, int k) { return (T * k + kPermChunk - 1) / kPermChunk;
 int launch_permute_many(const int* ids, int T, int k, int E, bool with_shared, int* bcnt, int* counts,
                         int* offsets, int* rows, int* tiles, int* tiles_n, int bm, hipStream_t st) {
   const int S = T * k, nb = permute_blocks(T, k);
-  permute_count<<<nb, 256, 0, st>>>(ids, S, E, bcnt);
+  permute_count<<<nb, kPermThreads, 0, st>>>(ids, S, E, bcnt);
   permute_plan<<<1, 1024, 0, st>>>(bcnt, nb, T, k, E, with_shared, counts, offsets, rows, tiles, tiles_n, bm);
-  permute_scatter<<<nb, 256, 0, st>>>(ids, S, E, bcnt, offsets, rows);
+  permute_scatter<<<nb, kPermThreads, 0, st>>>(ids, S, E, bcnt, offsets, rows);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 int launch_route_any(Args A, hipStream_t st, bool decode_sized, const LaunchHook& hook) {
   hipError_t err;
-  if (!decode_sized && A.act == MOE_BF16) {  // the prefill path's router and selection
+  if (!decode_sized) {  // the prefill path's router and selection (bf16 activations)
     const int rc = launch_pf_route(A, st, hook);
     if (rc) return rc;
   } else {
-    if (!A.logits_in) {
-      if (decode_sized) {  // the decode path's router kernel (no shared-expert blocks)
-        const int rc = launch_decode(A, st, /*route_only=*/true, hook);
-        if (rc) return rc;
-      } else {
-        dim3 grid((A.T + 63) / 64, (A.E + 63) / 64);
-        hook.pre("route_logits", st);
-        router_tiled<MOE_F32><<<grid, 256, 0, st>>>(A);
-        hook.post(st);
-        if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
-      }
+    if (!A.logits_in) {  // the decode path's router kernel (no shared-expert blocks)
+      const int rc = launch_decode(A, st, /*route_only=*/true, hook);
+      if (rc) return rc;
     }
     hook.pre("route_select", st);
     select_tokens<<<(A.T + 3) / 4, 256, 0, st>>>(A);
@@ -289,8 +261,7 @@ int launch_route_any(Args A, hipStream_t st, bool decode_sized, const LaunchHook
   }
   if (A.o_count || A.o_offset || A.o_sorted) {
     hook.pre("route_permute", st);
-    permute<<<1, 1024, 0, st>>>(A.ids, A.T, A.k, A.E, false, A.o_count, A.o_offset, A.o_sorted,
-                                nullptr, nullptr, 1);
+    permute<<<1, kPermThreads, 0, st>>>(A.ids, A.T, A.k, A.E, A.o_count, A.o_offset, A.o_sorted);
     hook.post(st);
     if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
   }

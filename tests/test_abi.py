@@ -108,8 +108,14 @@ def test_forward_argument_errors_enqueue_nothing(lib):
     assert _call_forward(s, w=w) == B.MOE_EINVAL
     w = B.Weights.from_buffer_copy(good); w.router_bias = 0x80000; w.bias_t_stride = 7
     assert _call_forward(s, w=w) == B.MOE_EINVAL
-    # MXFP4 needs its scale arrays
+    # MXFP4 needs its scale arrays, 16-byte aligned
     assert _call_forward(_shape(expert_dtype=2), w=good) == B.MOE_EINVAL
+    w = B.Weights.from_buffer_copy(good); w.gate_s, w.up_s, w.down_s = 0x90000, 0xA0000, 0xB0000
+    rc, need = _ws(_shape(expert_dtype=2, out_dtype=0))
+    assert _call_forward(_shape(expert_dtype=2, out_dtype=0), w=w, ws=None) == B.MOE_EWORKSPACE
+    for f in ("gate_s", "up_s", "down_s"):
+        wm = B.Weights.from_buffer_copy(w); setattr(wm, f, getattr(w, f) + 4)
+        assert _call_forward(_shape(expert_dtype=2, out_dtype=0), w=wm) == B.MOE_EALIGN, f
     # misaligned pointers
     assert _call_forward(s, x=0x1004) == B.MOE_EALIGN
     assert _call_forward(s, y=0x2002) == B.MOE_EALIGN
@@ -137,6 +143,22 @@ def test_route_argument_errors(lib):
     assert L.moe_route(ctypes.byref(s), None, ctypes.byref(w), None, ctypes.byref(out), 0x5000, 1 << 40, None) == B.MOE_EINVAL
     assert L.moe_route(ctypes.byref(s), 0x4000, ctypes.byref(w), None, ctypes.byref(out), None, 0, None) == B.MOE_EWORKSPACE
     assert L.moe_route(ctypes.byref(s), None, None, 0x6004, ctypes.byref(out), 0x5000, 1 << 40, None) == B.MOE_EALIGN
+
+
+def test_workspace_routing_offsets(lib):
+    """The forward pass's routing sits at the front of the workspace: logits [T][E] fp32, then
+    ids and weights [T][k], each section 256-byte aligned and inside the workspace."""
+    for kw in (dict(), dict(T=4, H=2560, E=512, I=768, I_shared=768), dict(T=4096),
+               dict(T=300, expert_dtype=2, out_dtype=0)):
+        s = _shape(**kw)
+        lo, io, wo = B.workspace_routing_offsets(s)
+        rc, need = _ws(s)
+        assert lo == 0 and io >= 4 * s.T * s.E and wo >= io + 4 * s.T * s.k
+        assert io % 256 == 0 and wo % 256 == 0 and wo + 4 * s.T * s.k <= need
+    n = ctypes.c_size_t(0)
+    assert B.lib().moe_workspace_routing(ctypes.byref(_shape()), None, ctypes.byref(n), ctypes.byref(n)) == B.MOE_EINVAL
+    assert B.lib().moe_workspace_routing(ctypes.byref(_shape(T=0)), ctypes.byref(n), ctypes.byref(n),
+                                         ctypes.byref(n)) == B.MOE_EINVAL
 
 
 def test_timing_api_rejects_misuse(lib):

@@ -186,6 +186,48 @@ def test_weights_equal_selected_ratio_and_sum_to_one(orc):
         assert np.all(np.diff(w) <= 0)
 
 
+def test_set_weights_are_the_softmax_of_the_set(orc):
+    """Renormalising the full softmax over a set equals the plain softmax of the set's own
+    logits (a library routine), in the order the set is given; shifting every logit by a
+    constant changes nothing; the 3/4 : 1/4 closed form; duplicate or out-of-range ids are
+    rejected."""
+    rng = np.random.default_rng(9)
+    for _ in range(200):
+        E = int(rng.integers(2, 80))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        l = (rng.standard_normal(E) * 3).astype(np.float32)
+        ids = rng.choice(E, k, replace=False).astype(np.int32)
+        w = orc.set_weights(l, ids)
+        assert np.allclose(w, scipy.special.softmax(l[ids].astype(np.float64)), rtol=1e-13, atol=0)
+        w2 = orc.set_weights((l.astype(np.float64) + 0.5).astype(np.float32), ids)
+        assert np.allclose(w, w2, rtol=1e-6, atol=0)
+    l = np.array([-50.0, math.log(3.0), 0.0, -50.0], np.float32)
+    r = math.exp(float(np.float32(math.log(3.0))))
+    w = orc.set_weights(l, [2, 1])
+    assert abs(w[0] - 1 / (r + 1)) < 1e-15 and abs(w[1] - r / (r + 1)) < 1e-15
+    for bad in ([1, 1], [0, 4], [-1, 2]):
+        with pytest.raises(ValueError):
+            orc.set_weights(l, bad)
+
+
+def test_near_tie_selections(orc):
+    """A token with no logit near its k-th admits exactly the oracle's selection; two logits
+    tied at the k-th place admit both choices, each with its own renormalised weights; a band
+    of three logits competing for two places admits the three pairs."""
+    l = np.array([4.0, 1.0, 3.0, 0.0, 2.0], np.float32)
+    sels = orc.near_tie_selections(l, 2)
+    assert len(sels) == 1 and sels[0][0].tolist() == [0, 2]
+    l = np.array([5.0, 2.0, 3.0, 3.0, 0.0], np.float32)
+    sels = orc.near_tie_selections(l, 2)
+    assert [s.tolist() for s, _ in sels] == [[0, 2], [0, 3]]
+    for s, w in sels:
+        assert np.allclose(w, scipy.special.softmax(l[s].astype(np.float64)), rtol=1e-13, atol=0)
+    l = np.array([1.0, 1.0 + 2e-6, 9.0, 1.0 + 4e-6], np.float32)
+    sels = orc.near_tie_selections(l, 3)
+    assert sorted(tuple(sorted(s.tolist())) for s, _ in sels) == [(0, 1, 2), (0, 2, 3), (1, 2, 3)]
+    assert all(s[0] == 2 for s, _ in sels)
+
+
 # --- permutation plan ---------------------------------------------------------------------
 
 def test_plan_histogram_2k_tokens(orc):
