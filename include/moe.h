@@ -61,6 +61,8 @@ extern "C" {
                                   arrays included)                              */
 #define MOE_EWORKSPACE (-4)    /* workspace null or smaller than required      */
 #define MOE_EHIP (-5)          /* a HIP runtime call or kernel launch failed   */
+#define MOE_ESCRATCH (-6)      /* moe_forward_static: the shape's workspace is
+                                  larger than MOE_STATIC_SCRATCH_BYTES          */
 
 /* Element encodings. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype_t;
@@ -153,6 +155,23 @@ int moe_route(const moe_shape_t *shape, const void *x, const moe_weights_t *w,
  */
 int moe_forward(const moe_shape_t *shape, const void *x, const moe_weights_t *w,
                 void *y, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_forward without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace is a
+ * static device array of MOE_STATIC_SCRATCH_BYTES that each GPU the library
+ * runs on holds until the process ends; shapes whose moe_workspace_size
+ * exceeds it are rejected with MOE_ESCRATCH before anything touches the
+ * device (every decode shape fits; prefill fits up to a few hundred tokens at
+ * the Qwen and Ling shapes).  Same kernels and results as moe_forward.  All
+ * calls on one GPU share its array: calls that may overlap on one GPU (two
+ * streams, two threads) race and must not be issued.  Nothing carries over
+ * from one call to the next.  Arguments, layouts and errors as moe_forward.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (32u << 20)
+int moe_forward_static(const moe_shape_t *shape, const void *x,
+                       const moe_weights_t *w, void *y, void *stream);
 
 /*
  * Where moe_forward leaves the routing it used, as byte offsets into its

@@ -10,10 +10,11 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
+STATIC_SCRATCH_BYTES = 32 << 20   # MOE_STATIC_SCRATCH_BYTES
 DTYPES = {"f32": 0, "bf16": 1, "mxfp4": 2}
-EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_workspace_routing", "moe_path_name",
-           "moe_strerror", "moe_timing_begin", "moe_timing_end")
+EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_static", "moe_workspace_routing",
+           "moe_path_name", "moe_strerror", "moe_timing_begin", "moe_timing_end")
 
 
 class Shape(ctypes.Structure):
@@ -63,6 +64,7 @@ def lib():
                                 ctypes.POINTER(RouteOut), P, ctypes.c_size_t, P]
         L.moe_forward.argtypes = [ctypes.POINTER(Shape), P, ctypes.POINTER(Weights), P, P,
                                   ctypes.c_size_t, P]
+        L.moe_forward_static.argtypes = [ctypes.POINTER(Shape), P, ctypes.POINTER(Weights), P, P]
         L.moe_workspace_routing.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t),
                                             ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
         L.moe_path_name.argtypes = [ctypes.POINTER(Shape)]
@@ -72,8 +74,8 @@ def lib():
         L.moe_timing_begin.argtypes = [ctypes.c_int32]
         L.moe_timing_end.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32,
                                      ctypes.POINTER(ctypes.c_int32)]
-        for n in ("moe_workspace_size", "moe_route", "moe_forward", "moe_workspace_routing", "moe_timing_begin",
-                  "moe_timing_end"):
+        for n in ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_static", "moe_workspace_routing",
+                  "moe_timing_begin", "moe_timing_end"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -158,6 +160,13 @@ def forward_routing(layer, ws):
     ids = ws[io:io + 4 * T * k].view(torch.int32).view(T, k)
     w = ws[wo:wo + 4 * T * k].view(torch.float32).view(T, k)
     return lg, ids, w
+
+
+def forward_static(shape: Shape, x, weights: Weights, y, stream=None) -> None:
+    """moe_forward_static: the layer with the library's static scratch as workspace."""
+    rc = lib().moe_forward_static(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(y), _stream(stream))
+    if rc:
+        raise MoeError(rc, "moe_forward_static")
 
 
 def path_name(shape: Shape) -> str:

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -172,6 +173,30 @@ LaunchHook hook() {
   return h;
 }
 
+// ---- static scratch for moe_forward_static ----------------------------------------------
+// One array per GPU the library runs on, held until the process ends.  In host code the name
+// `scratch` stands for the symbol, not for its device address: every kernel argument, fill or
+// copy uses the pointer hipGetSymbolAddress returned for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (looked up once per device, with that device current),
+// or null if the lookup fails.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -233,6 +258,21 @@ int moe_forward(const moe_shape_t* shape, const void* x, const moe_weights_t* w,
   return launch_prefill(A, (hipStream_t)stream, hook());
 }
 
+int moe_forward_static(const moe_shape_t* shape, const void* x, const moe_weights_t* w, void* y,
+                       void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (layout(shape).total > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ESCRATCH;  // before any device call
+  if (!x || !y) return MOE_EINVAL;
+  rc = check_weights(shape, w, true);
+  if (rc) return rc;
+  if (!aligned16(x) || !aligned16(y)) return MOE_EALIGN;
+  void* ws = scratch_ptr();
+  if (!ws) return MOE_EHIP;
+  // the kernels of moe_forward; the workspace needs no clearing (nothing carries across calls)
+  return moe_forward(shape, x, w, y, ws, (size_t)MOE_STATIC_SCRATCH_BYTES, stream);
+}
+
 int moe_workspace_routing(const moe_shape_t* shape, size_t* logits_off, size_t* ids_off, size_t* w_off) {
   int rc = check_shape(shape);
   if (rc) return rc;
@@ -263,6 +303,7 @@ const char* moe_strerror(int code) {
     case MOE_EALIGN: return "pointer not 16-byte aligned";
     case MOE_EWORKSPACE: return "workspace missing or too small";
     case MOE_EHIP: return "HIP runtime error or kernel launch failure";
+    case MOE_ESCRATCH: return "shape needs more workspace than the static scratch (MOE_STATIC_SCRATCH_BYTES)";
   }
   return "unknown error code";
 }

@@ -50,7 +50,7 @@ def _ws(shape):
 
 
 def test_strerror_covers_codes(lib):
-    for c in (0, -1, -2, -3, -4, -5):
+    for c in (0, -1, -2, -3, -4, -5, -6):
         assert B.strerror(c) and B.strerror(c) != "unknown error code"
     assert B.strerror(-99) == "unknown error code"
 
@@ -159,6 +159,25 @@ def test_workspace_routing_offsets(lib):
     assert B.lib().moe_workspace_routing(ctypes.byref(_shape()), None, ctypes.byref(n), ctypes.byref(n)) == B.MOE_EINVAL
     assert B.lib().moe_workspace_routing(ctypes.byref(_shape(T=0)), ctypes.byref(n), ctypes.byref(n),
                                          ctypes.byref(n)) == B.MOE_EINVAL
+
+
+def test_static_forward_rejects_oversized_shapes_before_the_device(lib):
+    """moe_forward_static refuses a shape whose workspace exceeds the static scratch with
+    MOE_ESCRATCH before any device call (so this runs without a GPU), and validates the
+    rest like moe_forward."""
+    w = B.Weights(0x10000, None, 0, 0x20000, 0x30000, 0x40000, None, None, None, 0x50000, 0x60000, 0x70000)
+    big = _shape(T=4096)
+    rc, need = _ws(big)
+    assert rc == 0 and need > B.STATIC_SCRATCH_BYTES
+    assert B.lib().moe_forward_static(ctypes.byref(big), 0x1000, ctypes.byref(w), 0x2000, None) == B.MOE_ESCRATCH
+    for kw in (dict(), dict(T=16, H=2560, E=512, I=768, I_shared=768),
+               dict(T=16, H=2560, E=512, I=768, I_shared=768, expert_dtype=2, out_dtype=0)):
+        rc, need = _ws(_shape(**kw))
+        assert rc == 0 and need <= B.STATIC_SCRATCH_BYTES, kw   # every decode shape of the workloads fits
+    s = _shape()
+    assert B.lib().moe_forward_static(ctypes.byref(s), None, ctypes.byref(w), 0x2000, None) == B.MOE_EINVAL
+    assert B.lib().moe_forward_static(ctypes.byref(s), 0x1004, ctypes.byref(w), 0x2000, None) == B.MOE_EALIGN
+    assert B.lib().moe_forward_static(ctypes.byref(_shape(T=0)), 0x1000, ctypes.byref(w), 0x2000, None) == B.MOE_EINVAL
 
 
 def test_timing_api_rejects_misuse(lib):
