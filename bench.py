@@ -10,83 +10,88 @@ experts), ling_mxfp4 (same with MXFP4 experts; T=1 or 4), qwen_prefill (T=4096),
 ling_mxfp4_prefill (T=4096, Ling shapes, MXFP4 experts, Zipf expert load).
 
 Prints ONE JSON line: value = tokens/s of the whole layer (inputs resident in HBM), the
-roofline of the dominant kernel (its algorithmic bytes per launch over its mean launch time
-from HIP events on the launch stream), and the CPU oracle timed on a bounded sample.
+layer's GB/s or TFLOP/s against the MI355X peaks and the measured read ceiling, the roofline
+of the dominant kernel (its algorithmic work per launch over its mean duration, both live:
+the library launches each kernel with hipExtLaunchKernel events tied to the kernel itself),
+and the CPU oracle timed on one pinned host core over a bounded sample.  The algorithmic work
+of the layer and of every kernel comes from routed_expert_ffn_route_amd/workmodel.py, the
+table the rocprofv3 summaries under profiles/ are computed from as well.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+from routed_expert_ffn_route_amd import workmodel as W  # noqa: E402
 
 
-def workload_spec(name, T_override=None, d=32):
-    if name == "qwen_decode":
-        return dict(T=T_override or 1, H=2048, E=256, k=8, I=512, I_shared=512, act="bf16", expert="bf16",
-                    shared="bf16", out="bf16", bias=None, d=None, layers=48)
-    if name == "ling_verify":
-        return dict(T=T_override or 4, H=2560, E=512, k=8, I=768, I_shared=768, act="bf16", expert="bf16",
-                    shared="bf16", out="bf16", bias="verify", d=d, layers=8)
-    if name == "ling_mxfp4":
-        T = T_override or 1
-        return dict(T=T, H=2560, E=512, k=8, I=768, I_shared=768, act="bf16", expert="mxfp4",
-                    shared="bf16", out="f32", bias=("verify" if T > 1 else None), d=(d if T > 1 else None),
-                    layers=48)
-    if name == "ling_mxfp4_prefill":
-        return dict(T=T_override or 4096, H=2560, E=512, k=8, I=768, I_shared=768, act="bf16", expert="mxfp4",
-                    shared="bf16", out="f32", bias="zipf", d=None, layers=8)
-    if name == "qwen_prefill":
-        return dict(T=T_override or 4096, H=2048, E=256, k=8, I=512, I_shared=512, act="bf16", expert="bf16",
-                    shared="bf16", out="bf16", bias="zipf", d=None, layers=8)
-    raise SystemExit(f"unknown workload {name}")
-
-
-def expert_bytes(spec):
-    """Bytes of one routed expert's gate+up and down weights."""
-    H, I = spec["H"], spec["I"]
-    if spec["expert"] == "mxfp4":
-        gu = 2 * (I * H // 2 + I * H // 32)
-        dn = H * I // 2 + H * I // 32
-    else:
-        es = 4 if spec["expert"] == "f32" else 2
-        gu, dn = 2 * I * H * es, H * I * es
-    return gu, dn
-
-
-def algorithmic_bytes(spec, distinct):
-    """Bytes the layer must move once: the distinct selected experts, the shared expert,
-    the fp32 router, x and y."""
-    H, E, T, Is = spec["H"], spec["E"], spec["T"], spec["I_shared"]
-    gu, dn = expert_bytes(spec)
-    ss = 2 if spec["shared"] == "bf16" else 4
-    shared = 3 * Is * H * ss
-    router = E * H * 4
-    xs = T * H * (2 if spec["act"] == "bf16" else 4)
-    ys = T * H * (2 if spec["out"] == "bf16" else 4)
-    return distinct * (gu + dn) + shared + router + xs + ys
-
-
-def traffic_from_profiles(kernel, workload, T):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
-    when there is none or the kernel's source changed since the counters were taken."""
+def profile_record(kernel, workload, T):
+    """The committed rocprofv3 summary of `kernel` on this workload (profiles/), if its kernel
+    sources still hash to the recorded value; else None."""
     from routed_expert_ffn_route_amd import profsum
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_T{T}.md")
     if not os.path.exists(path):
         return None
     for line in open(path):
-        if line.startswith("TRAFFIC_JSON:"):
+        if line.startswith("PROFILE_JSON:"):
             d = json.loads(line.split(":", 1)[1])
             if d.get("source_hash") == profsum.source_hash(kernel):
-                return d["traffic_bytes"]
+                return d
     return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(spec, layer_dev, seconds):
+    """The oracle (plain single-threaded C) on one pinned host core, on a bounded sample of the
+    workload: calls of up to 4 tokens (tokens are independent) on layer 0 with fresh seeded x,
+    until `seconds` have passed."""
+    import numpy as np
+
+    import oracle
+    from routed_expert_ffn_route_amd import synth
+    T = spec["T"]
+    Lh = synth.to_host(layer_dev)
+    Ts = min(T, 4)
+    Lh = Lh.with_T(Ts)
+    if Lh.router_bias is not None and Lh.bias_t_stride:
+        Lh.router_bias = np.ascontiguousarray(Lh.router_bias[:Ts])
+    aff = os.sched_getaffinity(0)
+    core = min(aff)
+    os.sched_setaffinity(0, {core})   # this thread only: the oracle runs here
+    try:
+        rng = np.random.default_rng(1234)
+        n, t0 = 0, time.perf_counter()
+        while True:
+            xr = rng.standard_normal((Ts, spec["H"]), dtype=np.float32)
+            xh = synth.f32_to_bf16_bits(xr) if spec["act"] == "bf16" else xr
+            oracle.forward(Lh, xh)
+            n += 1
+            if time.perf_counter() - t0 >= seconds and n >= 2:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, aff)
+    ncpu = os.cpu_count() or 1
+    return {"value": round(n * Ts / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "label": f"1 core of {ncpu}", "cpu": cpu_model(), "pinned_core": core,
+            "sample": f"{n} oracle calls of {Ts} token(s) each on layer 0 of the workload (fresh seeded x per "
+                      f"call), {dt:.1f} s on host core {core} (1 core of {ncpu}, {cpu_model()})"}
 
 
 def main():
@@ -103,6 +108,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -118,7 +124,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.lib()
-    spec = workload_spec(args.workload, args.T, args.d)
+    spec = W.workload_spec(args.workload, args.T, args.d)
     nl = args.layers or spec["layers"]
     T = spec["T"]
     print(f"# generating {nl} layers of {args.workload} on the device", file=sys.stderr, flush=True)
@@ -135,9 +141,9 @@ def main():
     y = torch.empty((T, spec["H"]), device="cuda",
                     dtype=torch.float32 if spec["out"] == "f32" else torch.int16)
     stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
 
-    # distinct experts per layer (for the bytes model), from the library's own routing
+    # distinct experts per layer (selected at decode, touched at prefill), from the library's
+    # own routing: the bytes model counts each distinct expert once
     distinct = []
     for Ld, xd, _ in layers:
         r = B.layer_route(Ld, xd)
@@ -153,7 +159,7 @@ def main():
         step(i, stream.cuda_stream)
     torch.cuda.synchronize()
 
-    def timed(fn):
+    def timed(fn, n):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -161,10 +167,10 @@ def main():
         fn()
         e1.record(torch.cuda.current_stream())
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+        return e0.elapsed_time(e1) / n
 
     # ---- eager: K back-to-back calls on the stream ----
-    ms_eager = timed(lambda: [step(i, stream.cuda_stream) for i in range(args.steps)])
+    ms_eager = timed(lambda: [step(i, stream.cuda_stream) for i in range(args.steps)], args.steps)
 
     # ---- graph: the same K calls captured once into a HIP graph and replayed ----
     ms_graph = None
@@ -176,84 +182,88 @@ def main():
                 step(i, cs.cuda_stream)
         g.replay()  # untimed
         torch.cuda.synchronize()
-        ms_graph = timed(g.replay)
+        ms_graph = timed(g.replay, args.steps)
     ms_step = ms_graph if ms_graph is not None else ms_eager
 
-    # ---- per-kernel durations: steps with every launch bracketed by HIP events on the launch
-    # stream.  A few fills of a 1 GiB buffer go first so that the host has queued every timed
-    # launch before the GPU reaches them: the intervals then hold GPU time only, not host gaps.
+    # ---- isolated latency: one call on an idle GPU (synchronised before and after) ----
+    iso = []
+    for i in range(min(args.steps, 30)):
+        iso.append(timed(lambda: step(i, stream.cuda_stream), 1))
+    us_isolated = statistics.median(iso) * 1e3
+
+    # ---- per-kernel durations: the library launches each kernel with hipExtLaunchKernel and a
+    # pair of events tied to that kernel's own start and end ----
     ksteps = min(args.steps, 20)
-    blocker = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
-    B.timing_begin(10 * ksteps)
-    with torch.cuda.stream(stream):
-        for _ in range(8):
-            blocker.fill_(1.0)
+    B.timing_begin(16 * ksteps)
     for i in range(ksteps):
         step(i, stream.cuda_stream)
     ktimes = B.timing_end()
     torch.cuda.synchronize()
-    del blocker
     kern = {n: (c, ms / c) for n, (c, ms) in ktimes.items()}
-    # an empty kernel bracketed the same way: reported beside the kernels (what the brackets
-    # cost with no work); the kernels' durations are the bracketed times as measured
-    ovh_ms = kern.pop("launch_overhead", (0, 0.0))[1]
     dom = max(kern, key=lambda n: kern[n][0] * kern[n][1])
-    dom_ms = kern[dom][1]
 
-    gu, dn = expert_bytes(spec)
-    H, I, Is, E, k = spec["H"], spec["I"], spec["I_shared"], spec["E"], spec["k"]
-    ss = 2 if spec["shared"] == "bf16" else 4
-    layer_bytes = algorithmic_bytes(spec, mean_distinct)
-    tok_s = T / (ms_step / 1e3)
-    layer_gbs = layer_bytes / (ms_step / 1e3) / 1e9
-    # algorithmic work of one launch of each kernel: bytes for the HBM-bound decode kernels,
-    # flops for the prefill GEMMs
-    work = {
-        "dec_router": ("hbm", E * H * 4),
-        "dec_select": ("hbm", 2 * Is * H * ss),  # the shared expert's gate/up rows (T > 1)
-        "dec_gateup": ("hbm", mean_distinct * gu + (2 * Is * H * ss if T == 1 else 0)),
-        "dec_down": ("hbm", mean_distinct * dn + Is * H * ss),  # + the shared expert's down rows
-        "pf_gateup": ("mfma", 2.0 * 2 * (T * k * I + T * Is) * H),
-        "pf_down": ("mfma", 2.0 * (T * k * I + T * Is) * H),
-        "pf_router": ("mfma", 2.0 * 3 * T * E * H),
-    }
+    work = W.kernel_work(spec, mean_distinct)
+    lbytes = W.layer_bytes(spec, mean_distinct)
+    lflops = W.layer_flops(spec)
+    t_s = ms_step / 1e3
+    tok_s = T / t_s
+    layer = {"bytes": int(lbytes), "flops": lflops, "gbs": round(lbytes / t_s / 1e9, 1),
+             "frac_hbm": round(lbytes / t_s / 1e9 / W.HBM_PEAK_GBS, 4),
+             "tflops": round(lflops / t_s / 1e12, 2),
+             "frac_mfma": round(lflops / t_s / 1e12 / W.BF16_MFMA_PEAK_TFLOPS, 4),
+             # the best the layer could do: bound by whichever of its flops and its bytes takes longer
+             "attainable_frac": round(max(lflops / (W.BF16_MFMA_PEAK_TFLOPS * 1e12),
+                                          lbytes / (W.HBM_PEAK_GBS * 1e9)) / t_s, 4)}
+
+    # ---- read ceiling: the same byte count per call streamed with the decode kernels' access
+    # pattern (16-byte loads over the whole chip), rotating through as many buffers as layers ----
+    ceil_gbs = None
+    if spec["T"] <= 16:
+        nbuf = min(nl, max(2, int(8e9 // max(lbytes, 1))))
+        per = (int(lbytes) + 255) // 256 * 256
+        big = torch.empty(nbuf * per, dtype=torch.uint8, device="cuda")
+        big.fill_(1)
+        sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+        for i in range(5):
+            B.read_ceiling(big[(i % nbuf) * per:], per, sink, stream.cuda_stream)
+        gc = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        with torch.cuda.graph(gc, stream=cs):
+            for i in range(args.steps):
+                B.read_ceiling(big[(i % nbuf) * per:], per, sink, cs.cuda_stream)
+        gc.replay()
+        torch.cuda.synchronize()
+        ms_read = timed(gc.replay, args.steps)
+        ceil_gbs = round(per / (ms_read / 1e3) / 1e9, 1)
+        layer["read_ceiling_gbs"] = ceil_gbs
+        layer["frac_of_read_ceiling"] = round(layer["gbs"] / ceil_gbs, 4)
+        del big, gc
+
+    # ---- roofline of the dominant kernel ----
     roof = None
     if dom in work:
-        bound, amount = work[dom]
-        if bound == "hbm":
-            ach, peak, unit = amount / (dom_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
+        wk = work[dom]
+        dom_s = kern[dom][1] / 1e3
+        if wk["bound"] == "hbm":
+            amount, ach, peak, unit = wk["bytes"], wk["bytes"] / dom_s / 1e9, W.HBM_PEAK_GBS, "GB/s"
         else:
-            ach, peak, unit = amount / (dom_ms / 1e3) / 1e12, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
-        roof = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
-                "frac": round(ach / peak, 4), "traffic": traffic_from_profiles(dom, args.workload, T),
-                "kernel": dom, "kernel_us": round(dom_ms * 1e3, 3),
-                "empty_launch_us": round(ovh_ms * 1e3, 3),
-                ("bytes_per_launch" if bound == "hbm" else "flops_per_launch"): int(amount)}
+            amount, ach, peak, unit = wk["flops"], wk["flops"] / dom_s / 1e12, W.BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
+        prof = profile_record(dom, args.workload, T)
+        roof = {"bound": wk["bound"], "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "traffic": prof["traffic_bytes"] if prof else None,
+                "kernel": dom, "kernel_us": round(kern[dom][1] * 1e3, 3),
+                ("bytes_per_launch" if wk["bound"] == "hbm" else "flops_per_launch"): int(amount),
+                "kernel_bytes_per_launch": wk["bytes"]}
+        if prof:  # the committed rocprofv3 mean of the same kernel source
+            roof["kernel_us_rocprof"] = round(prof["avg_ns"] / 1e3, 3)
+            roof["frac_rocprof"] = round(amount / (prof["avg_ns"] * 1e-9) / (1e9 if unit == "GB/s" else 1e12) / peak, 4)
+        if ceil_gbs and wk["bound"] == "hbm":
+            roof["frac_of_read_ceiling"] = round(ach / ceil_gbs, 4)
 
-    # ---- CPU baseline: the oracle, single-threaded, on a bounded sample of the workload ----
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        Lh = synth.to_host(layers[0][0])
-        Ts = min(T, 4)  # tokens are independent: the oracle runs a few at a time
-        Lh = Lh.with_T(Ts)
-        if Lh.router_bias is not None and Lh.bias_t_stride:
-            Lh.router_bias = np.ascontiguousarray(Lh.router_bias[:Ts])
-        n, t0 = 0, time.perf_counter()
-        rng = np.random.default_rng(1234)
-        while True:
-            xr = rng.standard_normal((Ts, spec["H"]), dtype=np.float32)
-            xh = synth.f32_to_bf16_bits(xr) if spec["act"] == "bf16" else xr
-            oracle.forward(Lh, xh)
-            n += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds and n >= 2:
-                break
-        dt = time.perf_counter() - t0
-        cpu = {"value": round(n * Ts / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n} oracle calls of {Ts} token(s) each on layer 0 of the workload "
-                         f"(fresh seeded x per call), {dt:.1f} s on one host thread"}
-        del Lh
+        cpu = cpu_baseline(spec, layers[0][0], args.cpu_seconds)
 
     if args.copy_calibration:
         a = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")
@@ -267,18 +277,24 @@ def main():
         "metric": "MoE layer tok/s + HBM GB/s (% of peak) at T=1/T=4 decode; TFLOP/s at prefill",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": spec["expert"], "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": spec["act"], "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "H": spec["H"], "E": spec["E"], "k": spec["k"],
-                   "I": spec["I"], "I_shared": spec["I_shared"], "layers_rotated": nl,
-                   "path": path, "distinct_experts_mean": mean_distinct},
+                   "I": spec["I"], "I_shared": spec["I_shared"], "weights": spec["expert"],
+                   "layers_rotated": min(nl, args.steps), "layers_drawn": nl, "path": path,
+                   "distinct_experts_mean": mean_distinct},
         "launch": "hipgraph" if ms_graph is not None else "eager",
-        "us_per_call_eager": round(ms_eager * 1e3, 3),
-        "layer_gbs": round(layer_gbs, 1), "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
-        "layer_bytes": int(layer_bytes), "us_per_call": round(ms_step * 1e3, 3),
+        "us_per_call": round(ms_step * 1e3, 3), "us_per_call_eager": round(ms_eager * 1e3, 3),
+        "us_isolated": round(us_isolated, 3),
+        "layer": layer,
         "kernels_us": {n: round(v[1] * 1e3, 3) for n, v in kern.items()},
+        "work": work,
         "roofline": roof, "cpu_baseline": cpu,
     }
-    print(json.dumps(out), flush=True)
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
 
 
 if __name__ == "__main__":

@@ -203,15 +203,16 @@ const char *moe_strerror(int code);
 /*
  * Kernel timing for measurement.  moe_timing_begin(n) creates n pairs of
  * HIP events (an allocation: call it outside any timed or captured region);
- * afterwards every kernel that moe_forward launches is bracketed by an event
- * pair on the call's stream until the pairs run out.  moe_timing_end()
- * synchronises those events, writes for each distinct kernel its name, the
- * number of timed launches and their summed duration in milliseconds
- * (up to max_out entries, *n_out set to the count), destroys the events and
- * turns timing off.  While timing is on, every moe_forward call also times one
- * empty kernel under the name "launch_overhead": what the event bracketing of
- * a launch costs with no work, to subtract from the kernels' durations.  Not
- * thread-safe; for benchmarks only.
+ * afterwards every kernel that moe_route / moe_forward launch takes the next
+ * pair and is launched with hipExtLaunchKernel, which records the kernel's own
+ * start and end in them (no marker packets between kernels), until the pairs
+ * run out.  moe_timing_end() synchronises those events, writes for each
+ * distinct kernel its name, the number of timed launches and their summed
+ * duration in milliseconds (up to max_out entries, *n_out set to the count),
+ * destroys the events and turns timing off.  Not thread-safe; for
+ * benchmarks only ("Optimizing on-device inference for Apple Silicon",
+ * section "Limits of further optimization": each kernel is measured against
+ * the rate its access pattern can sustain).
  */
 typedef struct {
   char name[64];
@@ -221,6 +222,18 @@ typedef struct {
 
 int moe_timing_begin(int32_t max_launches);
 int moe_timing_end(moe_kernel_time_t *out, int32_t max_out, int32_t *n_out);
+
+/*
+ * Read-rate probe for measurement: streams bytes (>= 16; the tail below a
+ * multiple of 16 is not read) of buf once with 16-byte loads spread over the
+ * whole chip, the access pattern of the decode kernels, and returns.  Timing
+ * it gives the sustained read ceiling the weight-streaming kernels are
+ * compared with ("Optimizing on-device inference for Apple Silicon", section
+ * "Limits of further optimization").  sink: 64 writable uint32 of device
+ * memory the kernel may write to (in practice it does not).  buf 16-byte
+ * aligned (MOE_EALIGN), null pointers MOE_EINVAL.
+ */
+int moe_read_ceiling(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

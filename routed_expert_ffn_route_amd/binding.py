@@ -14,7 +14,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP, MOE_
 STATIC_SCRATCH_BYTES = 32 << 20   # MOE_STATIC_SCRATCH_BYTES
 DTYPES = {"f32": 0, "bf16": 1, "mxfp4": 2}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_static", "moe_workspace_routing",
-           "moe_path_name", "moe_strerror", "moe_timing_begin", "moe_timing_end")
+           "moe_path_name", "moe_strerror", "moe_timing_begin", "moe_timing_end", "moe_read_ceiling")
 
 
 class Shape(ctypes.Structure):
@@ -74,8 +74,9 @@ def lib():
         L.moe_timing_begin.argtypes = [ctypes.c_int32]
         L.moe_timing_end.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32,
                                      ctypes.POINTER(ctypes.c_int32)]
+        L.moe_read_ceiling.argtypes = [P, ctypes.c_size_t, P, P]
         for n in ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_static", "moe_workspace_routing",
-                  "moe_timing_begin", "moe_timing_end"):
+                  "moe_timing_begin", "moe_timing_end", "moe_read_ceiling"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -186,6 +187,13 @@ def timing_end(max_out: int = 32) -> dict:
     if rc:
         raise MoeError(rc, "moe_timing_end")
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
+
+
+def read_ceiling(buf, nbytes: int, sink, stream=None) -> None:
+    """moe_read_ceiling: stream nbytes of buf once (the read-rate probe)."""
+    rc = lib().moe_read_ceiling(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
+    if rc:
+        raise MoeError(rc, "moe_read_ceiling")
 
 
 # Convenience on a synth.Layer of device tensors --------------------------------------------

@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 # (source, object, extra defines): decode_inst.hip is compiled once per dtype combination and
 # token tile so that the decode kernels build in parallel
 SOURCES = [("api.hip", "api.o", []), ("route.hip", "route.o", []), ("decode.hip", "decode.o", []),
-           ("prefill.hip", "prefill.o", [])] + [
+           ("prefill.hip", "prefill.o", []), ("measure.hip", "measure.o", [])] + [
     ("decode_inst.hip", f"decode_{n}_t{tm}.o", [f"-DMOE_DEC_NAME={n}", f"-DMOE_DEC_TM={tm}"])
     for n in ("fp4", "bf16", "f32") for tm in (1, 4, 8, 16)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -142,34 +142,20 @@ struct Timing {
   size_t used = 0;  // launches recorded
 } g_timing;
 
-void timing_pre(const char* name, hipStream_t st) {
-  if (!g_timing.on || g_timing.used >= g_timing.names.size()) return;
+// The next event pair for a launch (hipExtLaunchKernel records the kernel's start and end in
+// them), or false once the pairs are used up.
+bool timing_events(const char* name, hipEvent_t* e0, hipEvent_t* e1) {
+  if (!g_timing.on || g_timing.used >= g_timing.names.size()) return false;
   g_timing.names[g_timing.used] = name;
-  (void)hipEventRecord(g_timing.ev[2 * g_timing.used], st);
-}
-void timing_post(hipStream_t st) {
-  if (!g_timing.on || g_timing.used >= g_timing.names.size()) return;
-  (void)hipEventRecord(g_timing.ev[2 * g_timing.used + 1], st);
+  *e0 = g_timing.ev[2 * g_timing.used];
+  *e1 = g_timing.ev[2 * g_timing.used + 1];
   ++g_timing.used;
-}
-
-// Empty kernel timed beside the library's own while timing is on: the cost of one event-
-// bracketed launch with no work, which callers subtract from the kernels' durations.
-__global__ void timing_noop() {}
-
-void time_launch_overhead(hipStream_t st) {
-  if (!g_timing.on) return;
-  timing_pre("launch_overhead", st);
-  timing_noop<<<1, 64, 0, st>>>();
-  timing_post(st);
+  return true;
 }
 
 LaunchHook hook() {
   LaunchHook h;
-  if (g_timing.on) {
-    h.pre_fn = timing_pre;
-    h.post_fn = timing_post;
-  }
+  if (g_timing.on) h.events = timing_events;
   return h;
 }
 
@@ -253,7 +239,6 @@ int moe_forward(const moe_shape_t* shape, const void* x, const moe_weights_t* w,
   if (!aligned16(ws)) return MOE_EALIGN;
   Args A = make_args(shape, x, w, ws);
   A.y = y;
-  time_launch_overhead((hipStream_t)stream);
   if (shape->T <= kDecodeMaxT) return launch_decode(A, (hipStream_t)stream, false, hook());
   return launch_prefill(A, (hipStream_t)stream, hook());
 }
@@ -314,9 +299,7 @@ int moe_timing_begin(int32_t max_launches) {
   g_timing.ev.assign(2 * (size_t)max_launches, nullptr);
   g_timing.names.assign((size_t)max_launches, std::string());
   for (auto& e : g_timing.ev)
-    // no system-scope fence at each record: timing only, and a fence would add a cache
-    // write-back to every timed launch
-    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return MOE_EHIP;
+    if (hipEventCreate(&e) != hipSuccess) return MOE_EHIP;
   g_timing.used = 0;
   g_timing.on = true;
   return MOE_OK;

@@ -912,21 +912,13 @@ int gu_epc(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : 32; }
 int dn_epc(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : 32; }
 constexpr int kMaxLdsX = 64 * 1024;  // x staged in LDS by the gate/up kernels up to this size
 
-hipError_t launch_dyn(const void* f, dim3 grid, dim3 block, void** args, size_t lds, hipStream_t st) {
-  if (lds > 65536 && hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-    return hipErrorInvalidValue;
-  return hipLaunchKernel(f, grid, block, args, lds, st);
-}
-
 template <int XT, int WT, int SWT, int TM>
 int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& hook) {
   constexpr const GN* GUL = TM == 1 ? kGU1 : kGUn;
   const DevInfo dv = dev_info();
   const int S = A.T * A.k, D = S < A.E ? S : A.E;
   void* args1[] = {&A};
-  hook.pre("dec_router", st);
-  hipError_t err = hipLaunchKernel(router_fn<XT>(A.T), dim3(A.E), dim3(kThreads), args1, 0, st);
-  hook.post(st);
+  hipError_t err = launch(hook, "dec_router", router_fn<XT>(A.T), dim3(A.E), dim3(kThreads), args1, 0, st);
   if (err != hipSuccess) return MOE_EHIP;
   if (route_only) return MOE_OK;
 
@@ -942,9 +934,7 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   if (TM > 1) {
     void* fs = xl ? (void*)dec_select<XT, SWT, TM, true> : (void*)dec_select<XT, SWT, TM, false>;
     void* args_s[] = {&A, &nsh};
-    hook.pre("dec_select", st);
-    err = launch_dyn(fs, dim3(nsh + 1), dim3(kWave * TM), args_s, xl ? xbytes : 0, st);
-    hook.post(st);
+    err = launch(hook, "dec_select", fs, dim3(nsh + 1), dim3(kWave * TM), args_s, xl ? xbytes : 0, st);
     if (err != hipSuccess) return MOE_EHIP;
   }
 
@@ -959,9 +949,7 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   else
     f2 = xl ? gateup_fn<XT, WT, SWT, TM, GUL, true, false>(g2) : gateup_fn<XT, WT, SWT, TM, GUL, false, false>(g2);
   void* args2[] = {&A, &tiles, &sh_blocks};
-  hook.pre("dec_gateup", st);
-  err = launch_dyn(f2, dim3(sh_blocks + D * tiles), dim3(kThreads), args2, xl ? xbytes : 0, st);
-  hook.post(st);
+  err = launch(hook, "dec_gateup", f2, dim3(sh_blocks + D * tiles), dim3(kThreads), args2, xl ? xbytes : 0, st);
   if (err != hipSuccess) return MOE_EHIP;
 
   // down: at most one block per CU, each over an even share of the row groups
@@ -979,9 +967,7 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   const size_t lds3 = alds ? lds_act : (size_t)act_off * 4;
   void* f3 = alds ? down_fn<WT, SWT, TM, true>(g3) : down_fn<WT, SWT, TM, false>(g3);
   void* args3[] = {&A, &nrg, &nrgb, &act_off, &ash_off};
-  hook.pre("dec_down", st);
-  err = launch_dyn(f3, dim3(grid3), dim3(kWave * nw), args3, lds3, st);
-  hook.post(st);
+  err = launch(hook, "dec_down", f3, dim3(grid3), dim3(kWave * nw), args3, lds3, st);
   if (err != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }

@@ -1,24 +1,34 @@
 // Host-side launchers of the libmoe kernels (one per path) and the per-launch timing hook.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "common.h"
 
 namespace moe {
 
-// Called around every kernel launch; the API layer records HIP events here when kernel
-// timing is on (moe_timing_begin), and does nothing otherwise.
+// Kernel timing: while moe_timing_begin's events last, `events` hands each launch a pair of
+// HIP events and the kernel is launched with hipExtLaunchKernel, which ties them to the
+// kernel's own start and end (no marker packets between kernels, so the durations are the
+// kernels' alone).  Otherwise events is null and launches are plain.
 struct LaunchHook {
-  void (*pre_fn)(const char* name, hipStream_t st) = nullptr;
-  void (*post_fn)(hipStream_t st) = nullptr;
-  void pre(const char* name, hipStream_t st) const {
-    if (pre_fn) pre_fn(name, st);
-  }
-  void post(hipStream_t st) const {
-    if (post_fn) post_fn(st);
-  }
+  bool (*events)(const char* name, hipEvent_t* start, hipEvent_t* stop) = nullptr;
 };
+
+// Every kernel of the library is launched here (`name` labels it in the timing records).
+// Dynamic LDS above 64 KiB is enabled for the kernel first.
+inline hipError_t launch(const LaunchHook& hook, const char* name, const void* f, dim3 grid, dim3 block,
+                         void** args, size_t lds, hipStream_t st) {
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hook.events && hook.events(name, &e0, &e1))
+    return hipExtLaunchKernel(f, grid, block, args, lds, st, e0, e1, 0);
+  return hipLaunchKernel(f, grid, block, args, lds, st);
+}
 
 // Decode path (T <= kDecodeMaxT): router, selection/plan + shared gate/up, routed gate/up,
 // down + combine (shared and routed).  route_only stops after the router.
@@ -32,7 +42,8 @@ int launch_route_any(Args A, hipStream_t st, bool decode_sized, const LaunchHook
 // bcnt: workspace of permute_blocks(T, k) * E ints.
 int permute_blocks(int T, int k);
 int launch_permute_many(const int* ids, int T, int k, int E, bool with_shared, int* bcnt, int* counts,
-                        int* offsets, int* rows, int* tiles, int* tiles_n, int bm, hipStream_t st);
+                        int* offsets, int* rows, int* tiles, int* tiles_n, int bm, hipStream_t st,
+                        const LaunchHook& hook);
 
 // Router (MFMA, bf16 activations) + selection for T > kDecodeMaxT.
 int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook);

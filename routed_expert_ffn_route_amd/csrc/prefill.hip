@@ -652,22 +652,22 @@ __global__ __launch_bounds__(256) void pf_combine(Args A, PfLayout L) {
 // Router logits + per-token selection for T > 16 with bf16 activations (also used by
 // moe_route so that routing-only calls take the forward path's arithmetic).
 int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook) {
-  hipError_t err;
+  PfLayout L = pf_layout(A);
   if (!A.logits_in) {
-    const PfLayout L = pf_layout(A);
-    hook.pre("pf_router", st);
-    pf_split_router<<<256, 256, 0, st>>>(A, L.planes);
-    const int nbt = ((A.E + 63) / 64) * L.ks, tiles = (A.T + kPfBM - 1) / kPfBM;
-    const int nblocks = tiles * nbt;
-    pf_gemm<2, kPfBM, kPfNSG, MOE_BF16, false><<<nblocks, 2 * kPfBM, 0, st>>>(A, L, nbt, nblocks, 0);
-    hook.post(st);
-    if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
+    void* a1[] = {&A, &L.planes};
+    if (launch(hook, "pf_router_split", (const void*)pf_split_router, dim3(256), dim3(256), a1, 0, st) != hipSuccess)
+      return MOE_EHIP;
+    int nbt = ((A.E + 63) / 64) * L.ks, nblocks = ((A.T + kPfBM - 1) / kPfBM) * nbt, part = 0;
+    void* a2[] = {&A, &L, &nbt, &nblocks, &part};
+    if (launch(hook, "pf_router", (const void*)pf_gemm<2, kPfBM, kPfNSG, MOE_BF16, false>, dim3(nblocks),
+               dim3(2 * kPfBM), a2, 0, st) != hipSuccess)
+      return MOE_EHIP;
   }
-  const PfLayout L = pf_layout(A);
-  hook.pre("pf_select", st);
-  pf_select<<<(A.T + 3) / 4, 256, 0, st>>>(A, A.logits_in ? nullptr : L.rpart, L.ks);
-  hook.post(st);
-  if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
+  const float* rp = A.logits_in ? nullptr : L.rpart;
+  int ks = L.ks;
+  void* a3[] = {&A, &rp, &ks};
+  if (launch(hook, "pf_select", (const void*)pf_select, dim3((A.T + 3) / 4), dim3(256), a3, 0, st) != hipSuccess)
+    return MOE_EHIP;
   return MOE_OK;
 }
 
@@ -685,62 +685,53 @@ size_t pf_lds(int K) {
 }  // namespace
 
 int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
-  const PfLayout L = pf_layout(A);
-  hipError_t err;
+  PfLayout L = pf_layout(A);
   int rc = launch_pf_route(A, st, hook);
   if (rc) return rc;
-  hook.pre("pf_permute", st);
   rc = launch_permute_many(A.ids, A.T, A.k, A.E, A.Is > 0, L.bcnt, L.count, L.offset, L.rows, L.tiles,
-                           L.ntiles, kPfBM, st);
-  hook.post(st);
+                           L.ntiles, kPfBM, st, hook);
   if (rc) return rc;
   const int cap = prefill_tiles_cap(A.T, A.E, A.k);
   const int Imax = A.I > A.Is ? A.I : A.Is;
   const bool f4 = A.wdt == MOE_MXFP4;
   // MXFP4 experts: the routed groups' tiles run the MXFP4 kernel, the shared expert's tiles the
   // bf16 kernel, both in the precise variant (activation hi + lo parts, fp32 slot rows)
-  auto run = [&](const void* f, int nblocks, int nbt, int part, size_t lds) -> int {
-    if (lds > 65536 && hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return MOE_EHIP;
+  auto run = [&](const char* name, const void* f, int nblocks, int nbt, int part, size_t lds) -> int {
     PfLayout Lc = L;
     void* args[] = {&A, &Lc, &nbt, &nblocks, &part};
-    return hipLaunchKernel(f, dim3(nblocks), dim3(2 * kPfBM), args, lds, st) == hipSuccess ? MOE_OK : MOE_EHIP;
+    return launch(hook, name, f, dim3(nblocks), dim3(2 * kPfBM), args, lds, st) == hipSuccess ? MOE_OK : MOE_EHIP;
   };
   const int shtiles = A.Is > 0 ? (A.T + kPfBM - 1) / kPfBM : 0;
   {
     const int nbt = (Imax + kPfBN / 2 - 1) / (kPfBN / 2);
-    hook.pre("pf_gateup", st);
     if (!f4) {
-      rc = run((const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, false>, cap * nbt, nbt, 0, 0);
+      rc = run("pf_gateup", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, false>, cap * nbt, nbt, 0, 0);
     } else {
-      rc = run((const void*)pf_gemm<0, kPfBM, kPfNS, MOE_MXFP4, true>, cap * nbt, nbt, 1,
+      rc = run("pf_gateup", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_MXFP4, true>, cap * nbt, nbt, 1,
                pf_lds<0, kPfNS, MOE_MXFP4, true>(A.H));
       if (!rc && shtiles)
-        rc = run((const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, true>, shtiles * nbt, nbt, 2,
+        rc = run("pf_gateup_shared", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, true>, shtiles * nbt, nbt, 2,
                  pf_lds<0, kPfNS, MOE_BF16, true>(A.H));
     }
-    hook.post(st);
     if (rc) return rc;
   }
   {
     const int nbt = (A.H + kPfBN - 1) / kPfBN;
-    hook.pre("pf_down", st);
     if (!f4) {
-      rc = run((const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, false>, cap * nbt, nbt, 0, 0);
+      rc = run("pf_down", (const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, false>, cap * nbt, nbt, 0, 0);
     } else {
-      rc = run((const void*)pf_gemm<1, kPfBM, kPfNS, MOE_MXFP4, true>, cap * nbt, nbt, 1,
+      rc = run("pf_down", (const void*)pf_gemm<1, kPfBM, kPfNS, MOE_MXFP4, true>, cap * nbt, nbt, 1,
                pf_lds<1, kPfNS, MOE_MXFP4, true>(A.I));
       if (!rc && shtiles)
-        rc = run((const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, true>, shtiles * nbt, nbt, 2,
+        rc = run("pf_down_shared", (const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, true>, shtiles * nbt, nbt, 2,
                  pf_lds<1, kPfNSG, MOE_BF16, true>(A.Is));
     }
-    hook.post(st);
     if (rc) return rc;
   }
-  hook.pre("pf_combine", st);
-  pf_combine<<<(unsigned)(((size_t)A.T * (A.H / 8) + 255) / 256), 256, 0, st>>>(A, L);
-  hook.post(st);
-  if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
+  void* ac[] = {&A, &L};
+  if (launch(hook, "pf_combine", (const void*)pf_combine, dim3((unsigned)(((size_t)A.T * (A.H / 8) + 255) / 256)),
+             dim3(256), ac, 0, st) != hipSuccess)
+    return MOE_EHIP;
   return MOE_OK;
 }
 

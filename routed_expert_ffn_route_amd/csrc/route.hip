@@ -236,16 +236,24 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter(const int* ids, 
 int permute_blocks(int T, int k) { return (T * k + kPermChunk - 1) / kPermChunk; }
 
 int launch_permute_many(const int* ids, int T, int k, int E, bool with_shared, int* bcnt, int* counts,
-                        int* offsets, int* rows, int* tiles, int* tiles_n, int bm, hipStream_t st) {
-  const int S = T * k, nb = permute_blocks(T, k);
-  permute_count<<<nb, kPermThreads, 0, st>>>(ids, S, E, bcnt);
-  permute_plan<<<1, 1024, 0, st>>>(bcnt, nb, T, k, E, with_shared, counts, offsets, rows, tiles, tiles_n, bm);
-  permute_scatter<<<nb, kPermThreads, 0, st>>>(ids, S, E, bcnt, offsets, rows);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+                        int* offsets, int* rows, int* tiles, int* tiles_n, int bm, hipStream_t st,
+                        const LaunchHook& hook) {
+  int S = T * k, nb = permute_blocks(T, k);
+  void* a1[] = {&ids, &S, &E, &bcnt};
+  if (launch(hook, "pf_permute_count", (const void*)permute_count, dim3(nb), dim3(kPermThreads), a1, 0, st) !=
+      hipSuccess)
+    return MOE_EHIP;
+  void* a2[] = {&bcnt, &nb, &T, &k, &E, &with_shared, &counts, &offsets, &rows, &tiles, &tiles_n, &bm};
+  if (launch(hook, "pf_permute_plan", (const void*)permute_plan, dim3(1), dim3(1024), a2, 0, st) != hipSuccess)
+    return MOE_EHIP;
+  void* a3[] = {&ids, &S, &E, &bcnt, &offsets, &rows};
+  if (launch(hook, "pf_permute_scatter", (const void*)permute_scatter, dim3(nb), dim3(kPermThreads), a3, 0, st) !=
+      hipSuccess)
+    return MOE_EHIP;
+  return MOE_OK;
 }
 
 int launch_route_any(Args A, hipStream_t st, bool decode_sized, const LaunchHook& hook) {
-  hipError_t err;
   if (!decode_sized) {  // the prefill path's router and selection (bf16 activations)
     const int rc = launch_pf_route(A, st, hook);
     if (rc) return rc;
@@ -254,16 +262,15 @@ int launch_route_any(Args A, hipStream_t st, bool decode_sized, const LaunchHook
       const int rc = launch_decode(A, st, /*route_only=*/true, hook);
       if (rc) return rc;
     }
-    hook.pre("route_select", st);
-    select_tokens<<<(A.T + 3) / 4, 256, 0, st>>>(A);
-    hook.post(st);
-    if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
+    void* as[] = {&A};
+    if (launch(hook, "route_select", (const void*)select_tokens, dim3((A.T + 3) / 4), dim3(256), as, 0, st) !=
+        hipSuccess)
+      return MOE_EHIP;
   }
   if (A.o_count || A.o_offset || A.o_sorted) {
-    hook.pre("route_permute", st);
-    permute<<<1, kPermThreads, 0, st>>>(A.ids, A.T, A.k, A.E, A.o_count, A.o_offset, A.o_sorted);
-    hook.post(st);
-    if ((err = hipGetLastError()) != hipSuccess) return MOE_EHIP;
+    void* ap[] = {&A.ids, &A.T, &A.k, &A.E, &A.o_count, &A.o_offset, &A.o_sorted};
+    if (launch(hook, "route_permute", (const void*)permute, dim3(1), dim3(kPermThreads), ap, 0, st) != hipSuccess)
+      return MOE_EHIP;
   }
   return MOE_OK;
 }

@@ -180,6 +180,14 @@ def test_static_forward_rejects_oversized_shapes_before_the_device(lib):
     assert B.lib().moe_forward_static(ctypes.byref(_shape(T=0)), 0x1000, ctypes.byref(w), 0x2000, None) == B.MOE_EINVAL
 
 
+def test_read_ceiling_validates_arguments(lib):
+    L = B.lib()
+    assert L.moe_read_ceiling(None, 1024, 0x2000, None) == B.MOE_EINVAL
+    assert L.moe_read_ceiling(0x1000, 8, 0x2000, None) == B.MOE_EINVAL
+    assert L.moe_read_ceiling(0x1000, 1024, None, None) == B.MOE_EINVAL
+    assert L.moe_read_ceiling(0x1008, 1024, 0x2000, None) == B.MOE_EALIGN
+
+
 def test_timing_api_rejects_misuse(lib):
     assert B.lib().moe_timing_begin(0) == B.MOE_EINVAL
     n = ctypes.c_int32(0)
