@@ -22,8 +22,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, MXFP4 = 0, 1, 2
-_DTYPES = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4}
+F32, BF16, MXFP4, INT4G64 = 0, 1, 2, 3
+_DTYPES = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "int4g64": INT4G64}
 
 
 def build(force: bool = True) -> str:
@@ -46,7 +46,8 @@ class _Weights(ctypes.Structure):
                 ("bias_t_stride", ctypes.c_int64),
                 ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
                 ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p),
-                ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p)]
+                ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p),
+                ("gate_b", ctypes.c_void_p), ("up_b", ctypes.c_void_p), ("down_b", ctypes.c_void_p)]
 
 
 _lib = None
@@ -66,7 +67,7 @@ def lib():
         L.orc_e8m0_to_double.restype = ctypes.c_double
         L.orc_e8m0_to_double.argtypes = [ctypes.c_uint8]
         L.orc_weight.restype = ctypes.c_double
-        L.orc_weight.argtypes = [P, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+        L.orc_weight.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
         for name, args in {
             "orc_logits": [P, P, P, P],
@@ -107,7 +108,8 @@ def _weights(layer) -> tuple[_Weights, list]:
     w = _Weights(p(layer.router_w), p(layer.router_bias), layer.bias_t_stride,
                  p(layer.gate), p(layer.up), p(layer.down),
                  p(layer.gate_s), p(layer.up_s), p(layer.down_s),
-                 p(layer.sh_gate), p(layer.sh_up), p(layer.sh_down))
+                 p(layer.sh_gate), p(layer.sh_up), p(layer.sh_down),
+                 p(getattr(layer, "gate_b", None)), p(getattr(layer, "up_b", None)), p(getattr(layer, "down_b", None)))
     return w, keep
 
 
@@ -123,8 +125,8 @@ def e8m0_to_double(bits: int) -> float:
     return lib().orc_e8m0_to_double(bits)
 
 
-def weight(base: np.ndarray, scales, dtype: str, mat, rows, cols, r, c) -> float:
-    return lib().orc_weight(_ptr(base), _ptr(scales), _DTYPES[dtype], mat, rows, cols, r, c)
+def weight(base: np.ndarray, scales, dtype: str, mat, rows, cols, r, c, biases=None) -> float:
+    return lib().orc_weight(_ptr(base), _ptr(scales), _ptr(biases), _DTYPES[dtype], mat, rows, cols, r, c)
 
 
 def logits(layer, x: np.ndarray) -> np.ndarray:

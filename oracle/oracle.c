@@ -49,21 +49,27 @@ __attribute__((constructor)) static void fill_mx_tables(void) {
   for (int b = 0; b < 256; ++b) e8m0_table[b] = orc_e8m0_to_double((uint8_t)b);
 }
 
-double orc_weight(const void *base, const uint8_t *scales, int dtype,
-                  int64_t mat, int64_t rows, int64_t cols, int64_t r,
+double orc_weight(const void *base, const void *scales, const void *biases,
+                  int dtype, int64_t mat, int64_t rows, int64_t cols, int64_t r,
                   int64_t c) {
   int64_t row = mat * rows + r;
   if (dtype == ORC_F32) {
     return (double)((const float *)base)[row * cols + c];
   } else if (dtype == ORC_BF16) {
     return orc_bf16_to_double(((const uint16_t *)base)[row * cols + c]);
-  } else {
-    const uint8_t *codes = (const uint8_t *)base;
-    uint8_t byte = codes[row * (cols / 2) + c / 2];
-    uint8_t nib = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
-    uint8_t sc = scales[row * (cols / 32) + c / 32];
+  }
+  const uint8_t *codes = (const uint8_t *)base;
+  uint8_t byte = codes[row * (cols / 2) + c / 2];
+  uint8_t nib = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+  if (dtype == ORC_MXFP4) {
+    uint8_t sc = ((const uint8_t *)scales)[row * (cols / 32) + c / 32];
     return e2m1_table[nib] * e8m0_table[sc];
   }
+  /* ORC_INT4G64: s * q + b with the group's bf16 scale and bias */
+  int64_t g = row * (cols / 64) + c / 64;
+  double s = orc_bf16_to_double(((const uint16_t *)scales)[g]);
+  double b = orc_bf16_to_double(((const uint16_t *)biases)[g]);
+  return s * (double)nib + b;
 }
 
 static double act_value(const orc_shape *s, const void *x, int t, int h) {
@@ -75,6 +81,7 @@ static int shape_ok(const orc_shape *s) {
   if (s->T < 0 || s->H < 1 || s->E < 1 || s->k < 1 || s->k > s->E || s->I < 1 || s->I_shared < 0)
     return 0;
   if (s->expert_dtype == ORC_MXFP4 && (s->H % 32 != 0 || s->I % 32 != 0)) return 0;
+  if (s->expert_dtype == ORC_INT4G64 && (s->H % 64 != 0 || s->I % 64 != 0)) return 0;
   return 1;
 }
 
@@ -174,21 +181,22 @@ int orc_plan(const int32_t *ids, int T, int k, int E, int32_t *counts,
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 int orc_ffn(const double *xv, int H, int I, const void *g, const void *u,
-            const void *d, const uint8_t *gs, const uint8_t *us,
-            const uint8_t *ds, int dtype, int64_t mat, double *out) {
+            const void *d, const void *gs, const void *us, const void *ds,
+            const void *gb, const void *ub, const void *db, int dtype,
+            int64_t mat, double *out) {
   double *a = (double *)malloc(sizeof(double) * (size_t)I);
   if (!a) return -2;
   for (int i = 0; i < I; ++i) {
     double gi = 0.0, ui = 0.0;
     for (int h = 0; h < H; ++h) {
-      gi += orc_weight(g, gs, dtype, mat, I, H, i, h) * xv[h];
-      ui += orc_weight(u, us, dtype, mat, I, H, i, h) * xv[h];
+      gi += orc_weight(g, gs, gb, dtype, mat, I, H, i, h) * xv[h];
+      ui += orc_weight(u, us, ub, dtype, mat, I, H, i, h) * xv[h];
     }
     a[i] = silu(gi) * ui;
   }
   for (int h = 0; h < H; ++h) {
     double o = 0.0;
-    for (int i = 0; i < I; ++i) o += orc_weight(d, ds, dtype, mat, H, I, h, i) * a[i];
+    for (int i = 0; i < I; ++i) o += orc_weight(d, ds, db, dtype, mat, H, I, h, i) * a[i];
     out[h] = o;
   }
   free(a);
@@ -219,12 +227,12 @@ int orc_forward_with_routing(const orc_shape *s, const void *x,
         break;
       }
       rc = orc_ffn(xv, H, s->I, w->gate, w->up, w->down, w->gate_s, w->up_s,
-                   w->down_s, s->expert_dtype, e, o);
+                   w->down_s, w->gate_b, w->up_b, w->down_b, s->expert_dtype, e, o);
       for (int h = 0; h < H; ++h) yt[h] += cw[(int64_t)t * s->k + j] * o[h];
     }
     if (rc == 0 && s->I_shared > 0) {
       rc = orc_ffn(xv, H, s->I_shared, w->sh_gate, w->sh_up, w->sh_down, NULL,
-                   NULL, NULL, s->shared_dtype, 0, o);
+                   NULL, NULL, NULL, NULL, NULL, s->shared_dtype, 0, o);
       for (int h = 0; h < H; ++h) yt[h] += o[h];
     }
   }

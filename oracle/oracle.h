@@ -43,6 +43,14 @@
  *     contiguous).  MXFP4: two e2m1 codes per byte, the even element in the
  *     low nibble; one e8m0 scale byte per 32 consecutive elements of a row.
  *     e2m1 and e8m0 follow the OCP Microscaling (MX) v1.0 specification.
+ *  R6b group-wise affine 4-bit weights (same page, section "Decode weights
+ *     during matrix multiplication": each weight is a 4-bit integer code and
+ *     every group of 64 weights shares a bfloat16 scale and bias that
+ *     reconstruct its values): the code q is unsigned, 0..15, two per byte
+ *     with the even element in the low nibble; the groups are 64 consecutive
+ *     elements of a row along the reduction index; the weight is s*q + b,
+ *     taken exactly (the page's kernel rounds it to bfloat16 before its
+ *     multiply; that rounding belongs to the kernel, not to the weight).
  *  R7 routing plan: per-expert counts, exclusive offsets, and slots
  *     (slot = t*k + j) ordered by expert by a stable counting sort.
  *
@@ -60,12 +68,12 @@ extern "C" {
 #endif
 
 /* Element encodings understood by the oracle. */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2, ORC_INT4G64 = 3 };
 
 typedef struct {
   int32_t T, H, E, k, I, I_shared;
   int32_t act_dtype;    /* ORC_F32 | ORC_BF16 */
-  int32_t expert_dtype; /* ORC_F32 | ORC_BF16 | ORC_MXFP4 */
+  int32_t expert_dtype; /* ORC_F32 | ORC_BF16 | ORC_MXFP4 | ORC_INT4G64 */
   int32_t shared_dtype; /* ORC_F32 | ORC_BF16 */
 } orc_shape;
 
@@ -74,8 +82,10 @@ typedef struct {
   const float *router_bias;  /* NULL, [E] (stride 0) or [T][E] (stride E) */
   int64_t bias_t_stride;
   const void *gate, *up, *down;          /* [E][I][H], [E][I][H], [E][H][I] */
-  const uint8_t *gate_s, *up_s, *down_s; /* MXFP4 scales [E][I][H/32] ... */
+  const void *gate_s, *up_s, *down_s;    /* MXFP4: e8m0 bytes [E][I][H/32] ...;
+                                            INT4G64: bf16 scales [E][I][H/64] ... */
   const void *sh_gate, *sh_up, *sh_down; /* [Is][H], [Is][H], [H][Is] */
+  const void *gate_b, *up_b, *down_b;    /* INT4G64: bf16 biases [E][I][H/64] ... */
 } orc_weights;
 
 /* Scalar decoders (exact). */
@@ -85,8 +95,9 @@ double orc_e8m0_to_double(uint8_t bits);     /* 2^(bits-127); NaN for 0xFF */
 
 /* Element (row r, column c) of matrix `mat` of a stacked [n_mat][rows][cols]
  * weight array in the given encoding (cols is the reduction dimension). */
-double orc_weight(const void *base, const uint8_t *scales, int dtype,
-                  int64_t mat, int64_t rows, int64_t cols, int64_t r, int64_t c);
+double orc_weight(const void *base, const void *scales, const void *biases,
+                  int dtype, int64_t mat, int64_t rows, int64_t cols, int64_t r,
+                  int64_t c);
 
 /* R1: router logits for all tokens, fp32 [T][E]. */
 int orc_logits(const orc_shape *s, const void *x, const orc_weights *w,
@@ -108,8 +119,9 @@ int orc_plan(const int32_t *ids, int T, int k, int E, int32_t *counts,
 
 /* One SwiGLU FFN (R4) on one token vector: rows Wg/Wu [I][H], Wd [H][I]. */
 int orc_ffn(const double *xv, int H, int I, const void *g, const void *u,
-            const void *d, const uint8_t *gs, const uint8_t *us,
-            const uint8_t *ds, int dtype, int64_t mat, double *out);
+            const void *d, const void *gs, const void *us, const void *ds,
+            const void *gb, const void *ub, const void *db, int dtype,
+            int64_t mat, double *out);
 
 /* R4 + R5 with the routing given: y[T][H] (double). */
 int orc_forward_with_routing(const orc_shape *s, const void *x,

@@ -20,6 +20,13 @@ Workloads (shapes from the pages; values synthetic, no trained weights):
   T=1 (no bias) or T=4 (the verify bias recipe).
 * ``qwen_prefill`` T=4096 Qwen shapes, bf16, per-expert bias
   b_e = -1.1 * ln(pi(e) + 1) for a seeded permutation pi (Zipf-like load).
+* ``qwen_int4``   Qwen shapes with group-wise affine 4-bit experts ("Optimizing
+  on-device inference for Apple Silicon", section "Decode weights during
+  matrix multiplication": a 4-bit code per weight, a bf16 scale and bias per
+  64 weights): codes uniform over 0..15; per group s = (sigma / 3) * U[0.75,
+  1.25] and b = -7.5 * s * U[0.9, 1.1], sigma = 1/sqrt(fan_in), both rounded
+  to bf16 -- a group quantised from N(0, sigma^2) values spans about
+  +-2.5 sigma, so (max - min) / 15 and min land there.
 
 Distributions: x ~ N(0, 1); every weight ~ N(0, 1/fan_in) with fan_in = H for
 router, gate and up and I (or I_s) for down; fp32 -> bf16 by round to nearest
@@ -37,7 +44,7 @@ from typing import Optional
 
 import numpy as np
 
-BF16, F32, MXFP4 = "bf16", "f32", "mxfp4"
+BF16, F32, MXFP4, INT4 = "bf16", "f32", "mxfp4", "int4g64"
 
 
 @dataclasses.dataclass
@@ -58,19 +65,22 @@ class Layer:
     gate: object = None         # [E][I][H]   (bf16 as uint16 bits / fp32 / MXFP4 codes [E][I][H/2])
     up: object = None           # [E][I][H]
     down: object = None         # [E][H][I]
-    gate_s: object = None       # MXFP4 only: e8m0 [E][I][H/32]
+    gate_s: object = None       # MXFP4: e8m0 [E][I][H/32]; INT4: bf16 scales [E][I][H/64]
     up_s: object = None
-    down_s: object = None       # [E][H][I/32]
+    down_s: object = None       # [E][H][I/32] / [E][H][I/64]
     sh_gate: object = None      # [I_s][H]
     sh_up: object = None        # [I_s][H]
     sh_down: object = None      # [H][I_s]
+    gate_b: object = None       # INT4 only: bf16 biases [E][I][H/64]
+    up_b: object = None
+    down_b: object = None       # [E][H][I/64]
 
     def with_T(self, T: int) -> "Layer":
         return dataclasses.replace(self, T=T)
 
     def arrays(self):
         for f in ("router_w", "router_bias", "gate", "up", "down", "gate_s", "up_s", "down_s",
-                  "sh_gate", "sh_up", "sh_down"):
+                  "sh_gate", "sh_up", "sh_down", "gate_b", "up_b", "down_b"):
             yield f, getattr(self, f)
 
 
@@ -98,6 +108,14 @@ def _mxfp4(rng, E, N, K):
     codes = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
     scales = rng.integers(127 - 4, 127 + 3, size=(E, N, K // 32), dtype=np.uint8)
     return codes, scales
+
+
+def _int4(rng, E, N, K, std):
+    """Group-wise affine 4-bit weights: codes [E][N][K/2], bf16 scales and biases [E][N][K/64]."""
+    codes = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    s = (std / 3.0) * rng.uniform(0.75, 1.25, size=(E, N, K // 64))
+    b = -7.5 * s * rng.uniform(0.9, 1.1, size=(E, N, K // 64))
+    return codes, f32_to_bf16_bits(s.astype(np.float32)), f32_to_bf16_bits(b.astype(np.float32))
 
 
 def verify_bias(rng, T: int, E: int, k: int, d: int, boost: float = 8.0) -> np.ndarray:
@@ -148,6 +166,14 @@ def make_layer(T, H, E, k, I, I_shared, act=BF16, expert=BF16, shared=BF16, out=
             c, s_ = _mxfp4(rng, 1, H, I); dc.append(c); ds.append(s_)
         L.gate, L.up, L.down = np.concatenate(gc), np.concatenate(uc), np.concatenate(dc)
         L.gate_s, L.up_s, L.down_s = np.concatenate(gs), np.concatenate(us), np.concatenate(ds)
+    elif expert == INT4:
+        parts = {f: [] for f in ("gate", "gate_s", "gate_b", "up", "up_s", "up_b", "down", "down_s", "down_b")}
+        for _ in range(E):
+            for f, (n, kk, fan) in (("gate", (I, H, H)), ("up", (I, H, H)), ("down", (H, I, I))):
+                c, s_, b_ = _int4(rng, 1, n, kk, 1.0 / math.sqrt(fan))
+                parts[f].append(c); parts[f + "_s"].append(s_); parts[f + "_b"].append(b_)
+        for f, v in parts.items():
+            setattr(L, f, np.concatenate(v))
     else:
         shp_in, shp_out = (I, H), (H, I)
         gt = np.empty((E, I, H), np.float32 if expert == F32 else np.uint16)
@@ -216,15 +242,22 @@ def device_layer(T, H, E, k, I, I_shared, act=BF16, expert=BF16, shared=BF16, ou
     elif bias == "zipf":
         router_bias, stride = torch.from_numpy(zipf_bias(rng, E)).to(device), 0
     L = Layer(T, H, E, k, I, I_shared, act, expert, shared, out, router_w, router_bias, stride)
+    def codes(shape):
+        return torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.int32).to(torch.uint8)
     if expert == MXFP4:
-        def codes(shape):
-            return torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.int32).to(torch.uint8)
-
         def scales(shape):
             return torch.randint(123, 130, shape, generator=g, device=device, dtype=torch.int32).to(torch.uint8)
         L.gate, L.gate_s = codes((E, I, H // 2)), scales((E, I, H // 32))
         L.up, L.up_s = codes((E, I, H // 2)), scales((E, I, H // 32))
         L.down, L.down_s = codes((E, H, I // 2)), scales((E, H, I // 32))
+    elif expert == INT4:
+        def group_params(shape, std):  # the host recipe of _int4, drawn on the device
+            s = torch.empty(shape, device=device).uniform_(0.75, 1.25, generator=g).mul_(std / 3.0)
+            b = torch.empty(shape, device=device).uniform_(0.9, 1.1, generator=g).mul_(s).mul_(-7.5)
+            return s.to(torch.bfloat16).view(torch.int16), b.to(torch.bfloat16).view(torch.int16)
+        L.gate = codes((E, I, H // 2)); L.gate_s, L.gate_b = group_params((E, I, H // 64), 1.0 / math.sqrt(H))
+        L.up = codes((E, I, H // 2)); L.up_s, L.up_b = group_params((E, I, H // 64), 1.0 / math.sqrt(H))
+        L.down = codes((E, H, I // 2)); L.down_s, L.down_b = group_params((E, H, I // 64), 1.0 / math.sqrt(I))
     else:
         L.gate = torch.empty((E, I, H), device=device, dtype=torch.float32 if expert == F32 else torch.int16)
         L.up = torch.empty_like(L.gate)

@@ -87,6 +87,49 @@ def test_mxfp4_layout_nibble_order_and_scale_index(orc):
                 assert _same(got, want), (e, n, c)
 
 
+def test_int4_group_affine_closed_form(orc):
+    """Group-wise affine 4-bit: weight = s * q + b with q the unsigned nibble (element 2i in the
+    low nibble of byte i) and (s, b) the bf16 pair of the 64-element group the element falls in;
+    rows and experts stacked [E][N][K/2] and [E][N][K/64].  Hand-made bytes: one row of 128
+    elements, group 0 with s = 0.25, b = -1, group 1 with s = 2^-7, b = 3.5."""
+    codes = np.zeros((1, 1, 64), np.uint8)
+    codes[0, 0, 0] = 0x3A          # element 0 -> 10, element 1 -> 3
+    codes[0, 0, 31] = 0xF0         # element 62 -> 0, element 63 -> 15
+    codes[0, 0, 32] = 0x71         # element 64 -> 1, element 65 -> 7
+    codes[0, 0, 63] = 0x0C         # element 126 -> 12, element 127 -> 0
+    sc = synth.f32_to_bf16_bits(np.array([[[0.25, 2.0 ** -7]]], np.float32))
+    bi = synth.f32_to_bf16_bits(np.array([[[-1.0, 3.5]]], np.float32))
+    want = {0: 0.25 * 10 - 1, 1: 0.25 * 3 - 1, 62: -1.0, 63: 0.25 * 15 - 1, 64: 2.0 ** -7 + 3.5,
+            65: 7 * 2.0 ** -7 + 3.5, 126: 12 * 2.0 ** -7 + 3.5, 127: 3.5, 2: -1.0, 100: 3.5}
+    for c, v in want.items():
+        assert orc.weight(codes, sc, "int4g64", 0, 1, 128, 0, c, biases=bi) == v, c
+
+
+def test_int4_layout_and_roundtrip(orc):
+    """Every element of random stacked int4 weights equals s*q + b read off the bytes by index
+    arithmetic; and (w - b) / s recovers each of the 16 codes exactly for scales and biases of
+    the workloads' kind (quantise(dequantise(q)) == q)."""
+    E, N, K = 2, 3, 128
+    rng = np.random.default_rng(15)
+    codes, sc, bi = synth._int4(rng, E, N, K, 0.1)
+    for e in range(E):
+        for n in range(N):
+            for c in range(0, K, 3):
+                byte = int(codes[e, n, c // 2])
+                q = byte & 15 if c % 2 == 0 else byte >> 4
+                s_ = float(synth.bf16_bits_to_f32(sc[e, n, c // 64:c // 64 + 1])[0])
+                b_ = float(synth.bf16_bits_to_f32(bi[e, n, c // 64:c // 64 + 1])[0])
+                got = orc.weight(codes, sc, "int4g64", e, N, K, n, c, biases=bi)
+                assert got == s_ * q + b_, (e, n, c)
+                assert (got - b_) / s_ == q
+    for q in range(16):
+        row = np.full((1, 1, 32), q | (q << 4), np.uint8)
+        for s_, b_ in ((0.03125, -0.234375), (2.0 ** -9 * 3, -2.0 ** -5 * 11), (1.0, 0.0)):
+            w = orc.weight(row, synth.f32_to_bf16_bits(np.array([[[s_]]], np.float32)), "int4g64", 0, 1, 64, 0, 5,
+                           biases=synth.f32_to_bf16_bits(np.array([[[b_]]], np.float32)))
+            assert (w - b_) / s_ == q
+
+
 # --- router: logits, selection, weights -----------------------------------------------------
 
 def test_logits_exact_on_integer_inputs(orc):
@@ -280,6 +323,13 @@ def _np_mx(codes, scales):
     return vals * np.repeat(sc, 32, axis=-1)
 
 
+def _np_int4(codes, sc, bi):
+    q = np.stack([codes & 15, codes >> 4], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
+    s_ = synth.bf16_bits_to_f32(sc).astype(np.float64)
+    b_ = synth.bf16_bits_to_f32(bi).astype(np.float64)
+    return q * np.repeat(s_, 64, axis=-1) + np.repeat(b_, 64, axis=-1)
+
+
 def _np_ffn(xv, Wg, Wu, Wd):
     g = Wg @ xv
     u = Wu @ xv
@@ -287,7 +337,7 @@ def _np_ffn(xv, Wg, Wu, Wd):
     return Wd @ a
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "mxfp4"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "mxfp4", "int4g64"])
 def test_single_expert_is_dense_swiglu(orc, dtype):
     """E = 1, k = 1, no shared expert: the layer is a dense SwiGLU FFN."""
     act = "f32" if dtype == "f32" else "bf16"
@@ -297,6 +347,9 @@ def test_single_expert_is_dense_swiglu(orc, dtype):
     xs = _np_w(x, act)
     if dtype == "mxfp4":
         Wg, Wu, Wd = _np_mx(L.gate, L.gate_s)[0], _np_mx(L.up, L.up_s)[0], _np_mx(L.down, L.down_s)[0]
+    elif dtype == "int4g64":
+        Wg, Wu, Wd = (_np_int4(L.gate, L.gate_s, L.gate_b)[0], _np_int4(L.up, L.up_s, L.up_b)[0],
+                      _np_int4(L.down, L.down_s, L.down_b)[0])
     else:
         Wg, Wu, Wd = _np_w(L.gate[0], dtype), _np_w(L.up[0], dtype), _np_w(L.down[0], dtype)
     for t in range(3):
