@@ -33,6 +33,13 @@
  *   MXFP4    two e2m1 codes per byte, element 2i in the low nibble; one e8m0
  *            scale byte per 32 consecutive elements of a row:
  *            gate_s, up_s [E][I][H/32], down_s [E][H][I/32]  (OCP MX v1.0)
+ *   INT4G64  group-wise affine 4-bit ("Optimizing on-device inference for
+ *            Apple Silicon", section "Decode weights during matrix
+ *            multiplication": a 4-bit integer code per weight, a bfloat16
+ *            scale and bias per 64 weights): unsigned codes q in 0..15 packed
+ *            like MXFP4; per 64 consecutive elements of a row one bf16 scale s
+ *            and one bf16 bias b, weight = s * q + b:
+ *            gate_s/gate_b, up_s/up_b [E][I][H/64], down_s/down_b [E][H][I/64]
  *   sh_gate, sh_up [I_shared][H], sh_down [H][I_shared]   shared_dtype
  *   y        [T][H]          out_dtype
  *
@@ -65,7 +72,7 @@ extern "C" {
                                   larger than MOE_STATIC_SCRATCH_BYTES          */
 
 /* Element encodings. */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype_t;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2, MOE_INT4G64 = 3 } moe_dtype_t;
 
 /* Limits checked by every entry point. */
 #define MOE_MAX_E 1024     /* routed experts                                   */
@@ -77,13 +84,13 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype_t;
 
 typedef struct {
   int32_t T;            /* tokens, >= 1                                        */
-  int32_t H;            /* hidden size, multiple of 32                         */
+  int32_t H;            /* hidden size, multiple of 32 (INT4G64: of 64)        */
   int32_t E;            /* routed experts, 1..MOE_MAX_E                        */
   int32_t k;            /* experts per token, 1..min(E, MOE_MAX_K)             */
-  int32_t I;            /* routed intermediate size, multiple of 32            */
+  int32_t I;            /* routed intermediate size, multiple of 32 (INT4G64: of 64) */
   int32_t I_shared;     /* shared intermediate size, multiple of 32; 0 = none  */
   int32_t act_dtype;    /* x:          MOE_F32 | MOE_BF16                      */
-  int32_t expert_dtype; /* gate/up/down: MOE_F32 | MOE_BF16 | MOE_MXFP4        */
+  int32_t expert_dtype; /* gate/up/down: MOE_F32 | MOE_BF16 | MOE_MXFP4 | MOE_INT4G64 */
   int32_t shared_dtype; /* shared expert: MOE_F32 | MOE_BF16                   */
   int32_t out_dtype;    /* y:          MOE_F32 | MOE_BF16                      */
 } moe_shape_t;
@@ -94,8 +101,11 @@ typedef struct {
                                 [T][E] if bias_t_stride == E                   */
   int64_t bias_t_stride;
   const void *gate, *up, *down;          /* required                           */
-  const uint8_t *gate_s, *up_s, *down_s; /* required iff expert_dtype MXFP4    */
+  const void *gate_s, *up_s, *down_s;    /* MXFP4: e8m0 scale bytes; INT4G64:
+                                            bf16 group scales; else unused     */
   const void *sh_gate, *sh_up, *sh_down; /* required iff I_shared > 0          */
+  const void *gate_b, *up_b, *down_b;    /* INT4G64: bf16 group biases; else
+                                            unused                             */
 } moe_weights_t;
 
 typedef struct {          /* outputs of moe_route; ids and w required         */

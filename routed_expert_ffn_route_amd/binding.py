@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 STATIC_SCRATCH_BYTES = 32 << 20   # MOE_STATIC_SCRATCH_BYTES
-DTYPES = {"f32": 0, "bf16": 1, "mxfp4": 2}
+DTYPES = {"f32": 0, "bf16": 1, "mxfp4": 2, "int4g64": 3}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_static", "moe_workspace_routing",
            "moe_path_name", "moe_strerror", "moe_timing_begin", "moe_timing_end", "moe_read_ceiling")
 
@@ -28,7 +28,8 @@ class Weights(ctypes.Structure):
                 ("bias_t_stride", ctypes.c_int64),
                 ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
                 ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p),
-                ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p)]
+                ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p),
+                ("gate_b", ctypes.c_void_p), ("up_b", ctypes.c_void_p), ("down_b", ctypes.c_void_p)]
 
 
 class RouteOut(ctypes.Structure):
@@ -102,7 +103,8 @@ def weights_of(layer) -> Weights:
     return Weights(_ptr(layer.router_w), _ptr(layer.router_bias), layer.bias_t_stride,
                    _ptr(layer.gate), _ptr(layer.up), _ptr(layer.down),
                    _ptr(layer.gate_s), _ptr(layer.up_s), _ptr(layer.down_s),
-                   _ptr(layer.sh_gate), _ptr(layer.sh_up), _ptr(layer.sh_down))
+                   _ptr(layer.sh_gate), _ptr(layer.sh_up), _ptr(layer.sh_down),
+                   _ptr(layer.gate_b), _ptr(layer.up_b), _ptr(layer.down_b))
 
 
 def _stream(stream):

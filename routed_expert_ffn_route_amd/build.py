@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = [("api.hip", "api.o", []), ("route.hip", "route.o", []), ("decode.hip", "decode.o", []),
            ("prefill.hip", "prefill.o", []), ("measure.hip", "measure.o", [])] + [
     ("decode_inst.hip", f"decode_{n}_t{tm}.o", [f"-DMOE_DEC_NAME={n}", f"-DMOE_DEC_TM={tm}"])
-    for n in ("fp4", "bf16", "f32") for tm in (1, 4, 8, 16)]
+    for n in ("fp4", "i4", "bf16", "f32") for tm in (1, 4, 8, 16)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-Wno-unused-variable",

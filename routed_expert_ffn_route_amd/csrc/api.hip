@@ -31,14 +31,17 @@ int check_shape(const moe_shape_t* s) {
   if (s->H % 32 || s->I % 32 || s->I_shared % 32) return MOE_EUNSUPPORTED;
   const bool f32 = s->act_dtype == MOE_F32 && s->expert_dtype == MOE_F32 && s->shared_dtype == MOE_F32;
   const bool b16 = s->act_dtype == MOE_BF16 &&
-                   (s->expert_dtype == MOE_BF16 || s->expert_dtype == MOE_MXFP4) &&
+                   (s->expert_dtype == MOE_BF16 || s->expert_dtype == MOE_MXFP4 ||
+                    s->expert_dtype == MOE_INT4G64) &&
                    s->shared_dtype == MOE_BF16;
   if (!f32 && !b16) return MOE_EUNSUPPORTED;
+  if (s->expert_dtype == MOE_INT4G64 && (s->H % 64 || s->I % 64)) return MOE_EUNSUPPORTED;
   if (s->out_dtype != MOE_F32 && s->out_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
   if (s->T > kDecodeMaxT) {  // prefill path
     if (s->act_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
-    // MXFP4 experts: the scale rows of a 256-row weight tile are staged in LDS (K / 32 <= 256)
-    if (s->expert_dtype == MOE_MXFP4 && (s->H > 8192 || s->I > 8192)) return MOE_EUNSUPPORTED;
+    // MXFP4 / INT4G64 experts: the scale (and bias) rows of a weight tile are staged in LDS
+    if ((s->expert_dtype == MOE_MXFP4 || s->expert_dtype == MOE_INT4G64) && (s->H > 8192 || s->I > 8192))
+      return MOE_EUNSUPPORTED;
     if ((size_t)s->T * s->H * 2 >= ((size_t)1 << 31)) return MOE_EUNSUPPORTED;  // 32-bit row offsets
   }
   return MOE_OK;
@@ -68,7 +71,8 @@ Layout layout(const moe_shape_t* s) {
     off += up(S * (size_t)s->I * 4);
   } else {
     L.pf = off;
-    off += up(prefill_ws_bytes(s->T, s->H, s->E, s->k, s->I, s->I_shared, s->expert_dtype == MOE_MXFP4));
+    off += up(prefill_ws_bytes(s->T, s->H, s->E, s->k, s->I, s->I_shared,
+                               s->expert_dtype == MOE_MXFP4 || s->expert_dtype == MOE_INT4G64));
   }
   L.total = off;
   return L;
@@ -100,6 +104,9 @@ Args make_args(const moe_shape_t* s, const void* x, const moe_weights_t* w, void
   A.sgate = w->sh_gate;
   A.sup = w->sh_up;
   A.sdown = w->sh_down;
+  A.gb = w->gate_b;
+  A.ub = w->up_b;
+  A.db = w->down_b;
   const Layout L = layout(s);
   uint8_t* b = (uint8_t*)ws;
   A.logits = (float*)(b + L.logits);
@@ -121,14 +128,22 @@ int check_weights(const moe_shape_t* s, const moe_weights_t* w, bool experts) {
   if (!aligned16(w->router_w)) return MOE_EALIGN;
   if (!experts) return MOE_OK;
   if (!w->gate || !w->up || !w->down) return MOE_EINVAL;
-  if (s->expert_dtype == MOE_MXFP4 && (!w->gate_s || !w->up_s || !w->down_s)) return MOE_EINVAL;
+  if ((s->expert_dtype == MOE_MXFP4 || s->expert_dtype == MOE_INT4G64) && (!w->gate_s || !w->up_s || !w->down_s))
+    return MOE_EINVAL;
+  if (s->expert_dtype == MOE_INT4G64 && (!w->gate_b || !w->up_b || !w->down_b)) return MOE_EINVAL;
   if (s->I_shared > 0 && (!w->sh_gate || !w->sh_up || !w->sh_down)) return MOE_EINVAL;
   const void* ptrs[] = {w->gate, w->up, w->down, w->sh_gate, w->sh_up, w->sh_down};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_EALIGN;
-  if (s->expert_dtype == MOE_MXFP4) {  // the grouped GEMM stages scale rows with 16-byte loads
+  if (s->expert_dtype == MOE_MXFP4 || s->expert_dtype == MOE_INT4G64) {
+    // the grouped GEMM stages scale (and bias) rows with 16-byte loads
     const void* sc[] = {w->gate_s, w->up_s, w->down_s};
     for (const void* p : sc)
+      if (!aligned16(p)) return MOE_EALIGN;
+  }
+  if (s->expert_dtype == MOE_INT4G64) {
+    const void* bi[] = {w->gate_b, w->up_b, w->down_b};
+    for (const void* p : bi)
       if (!aligned16(p)) return MOE_EALIGN;
   }
   return MOE_OK;
@@ -276,6 +291,7 @@ const char* moe_path_name(const moe_shape_t* shape) {
     case MOE_F32: return dec ? "decode.f32" : "prefill.f32";
     case MOE_BF16: return dec ? "decode.bf16" : "prefill.bf16";
     case MOE_MXFP4: return dec ? "decode.mxfp4" : "prefill.mxfp4";
+    case MOE_INT4G64: return dec ? "decode.int4g64" : "prefill.int4g64";
   }
   return "invalid";
 }

@@ -22,8 +22,9 @@ struct Args {
   const float* rbias;
   long long bias_stride;
   const void *gate, *up, *down;
-  const uint8_t *gs, *us, *ds;
+  const void *gs, *us, *ds;           // MXFP4: e8m0 bytes; INT4G64: bf16 group scales
   const void *sgate, *sup, *sdown;
+  const void *gb, *ub, *db;           // INT4G64: bf16 group biases
   void* y;
   // route-only inputs/outputs (moe_route); null in moe_forward
   const float* logits_in;

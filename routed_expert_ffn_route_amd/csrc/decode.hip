@@ -18,11 +18,13 @@ namespace moe {
 MOE_DECL(f32)
 MOE_DECL(bf16)
 MOE_DECL(fp4)
+MOE_DECL(i4)
 #undef MOE_DECL
 
 int launch_decode(Args A, hipStream_t st, bool route_only, const LaunchHook& hook) {
   if (A.act == MOE_F32) return launch_decode_f32(A, st, route_only, hook);
   if (A.wdt == MOE_MXFP4) return launch_decode_fp4(A, st, route_only, hook);
+  if (A.wdt == MOE_INT4G64) return launch_decode_i4(A, st, route_only, hook);
   return launch_decode_bf16(A, st, route_only, hook);
 }
 

@@ -41,6 +41,7 @@ template <int WT> struct GU;
 template <> struct GU<MOE_F32> { static constexpr int EPC = 4; };
 template <> struct GU<MOE_BF16> { static constexpr int EPC = 8; };
 template <> struct GU<MOE_MXFP4> { static constexpr int EPC = 32; };
+template <> struct GU<MOE_INT4G64> { static constexpr int EPC = 32; };
 
 template <int XT> struct XS;
 template <> struct XS<MOE_F32> { static constexpr int BYTES = 4; };
@@ -122,6 +123,57 @@ template <> struct GUC<MOE_MXFP4, MOE_BF16> {
   }
 };
 
+// Group-wise affine 4-bit (a code q in 0..15 per weight, a bf16 scale s and bias b per 64):
+// a chunk is 32 codes, half a group.  Each code pair becomes the bf16 pair (128 + q0, 128 + q1)
+// (exact: bf16 holds the integers 128..143), so one dot2 per pair gives D = sum x (128 + q),
+// and sum x (s q + b) = s D + (b - 128 s) X with X = sum x over the chunk.
+template <> struct GUC<MOE_INT4G64, MOE_BF16> {
+  struct D { uint32_t v[16]; };
+  // code pair j of dword w (elements 2j, 2j + 1) -> bf16 pair 128 + q: byte j of w and byte j
+  // of w >> 4 (whose low nibble is the high code) land in the two halves, then the exponent
+  static __device__ __forceinline__ void deq4(uint32_t w, uint32_t* o) {
+    const uint32_t w4 = w >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t sel = (uint32_t)j | 0x0C00u | ((uint32_t)(4 + j) << 16) | 0x0C000000u;
+      o[j] = (__builtin_amdgcn_perm(w4, w, sel) & 0x000F000Fu) | 0x43004300u;
+    }
+  }
+  static __device__ __forceinline__ D deq(uint4 w) {
+    D d;
+    deq4(w.x, d.v);
+    deq4(w.y, d.v + 4);
+    deq4(w.z, d.v + 8);
+    deq4(w.w, d.v + 12);
+    return d;
+  }
+  // sg, su: the scales (0 for a masked chunk); cg, cu: b - 128 s
+  static __device__ __forceinline__ void dot(const D& g, const D& u, const uint8_t* xrow, int c, float sg,
+                                             float cg, float su, float cu, float& ag, float& au) {
+    const uint8_t* xp = xrow + (size_t)c * 64;
+    float a = 0.f, b = 0.f, x = 0.f;
+    constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 xv = ldg16(xp + 16 * q);
+      a = dot2_bf16(g.v[4 * q + 0], xv.x, a);
+      b = dot2_bf16(u.v[4 * q + 0], xv.x, b);
+      x = dot2_bf16(kOnes, xv.x, x);
+      a = dot2_bf16(g.v[4 * q + 1], xv.y, a);
+      b = dot2_bf16(u.v[4 * q + 1], xv.y, b);
+      x = dot2_bf16(kOnes, xv.y, x);
+      a = dot2_bf16(g.v[4 * q + 2], xv.z, a);
+      b = dot2_bf16(u.v[4 * q + 2], xv.z, b);
+      x = dot2_bf16(kOnes, xv.z, x);
+      a = dot2_bf16(g.v[4 * q + 3], xv.w, a);
+      b = dot2_bf16(u.v[4 * q + 3], xv.w, b);
+      x = dot2_bf16(kOnes, xv.w, x);
+    }
+    ag = fmaf(sg, a, fmaf(cg, x, ag));
+    au = fmaf(su, b, fmaf(cu, x, au));
+  }
+};
+
 // Copying x rows into LDS: the block's threads take 16-byte units of the rows of the tokens in
 // `mask` (compacted: unit i lies in the (i / rw)-th token of the mask), kXB units per thread
 // per pass, all loads of a pass issued before any store (a load-store loop would wait a full
@@ -168,8 +220,8 @@ __device__ __forceinline__ void x_rows_store(const uint4 (&xr)[kXB], int base, i
 // call this function with the same mask.
 template <int XT, int WT, int G, int NCH, int TM, bool XL>
 __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* urow,
-                                           const uint8_t* gsrow, const uint8_t* usrow,
-                                           int nchunks, const uint8_t* xg, uint4* xs, int xbytes,
+                                           const void* gsrow, const void* usrow, const void* gbrow,
+                                           const void* ubrow, int nchunks, const uint8_t* xg, uint4* xs, int xbytes,
                                            size_t xstride, unsigned mask, const int* slots,
                                            float* out, int out_ld, int row, int gl, bool valid) {
   typedef GUC<WT, XT> C;
@@ -181,7 +233,8 @@ __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* u
   if constexpr (XL) x_rows_load(xr, threadIdx.x, xn, rw, mask, xg, xstride);
   for (int c0 = 0; c0 < nchunks; c0 += G * NCH) {
     uint4 wg[NCH], wu[NCH];
-    uint32_t bg[NCH], bu[NCH];  // e2m1: raw scale bytes, converted when the chunk is used
+    uint32_t bg[NCH], bu[NCH];  // raw scales (e8m0 byte; int4: bf16 bias << 16 | bf16 scale), converted
+                                // when the chunk is used
     float okf[NCH];
     int cc[NCH];
 #pragma unroll
@@ -193,8 +246,11 @@ __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* u
       wg[m] = ldg16(grow + (size_t)cc[m] * 16);
       wu[m] = ldg16(urow + (size_t)cc[m] * 16);
       if constexpr (WT == MOE_MXFP4) {
-        bg[m] = gsrow[cc[m]];
-        bu[m] = usrow[cc[m]];
+        bg[m] = ((const uint8_t*)gsrow)[cc[m]];
+        bu[m] = ((const uint8_t*)usrow)[cc[m]];
+      } else if constexpr (WT == MOE_INT4G64) {  // the chunk's group: two chunks per 64 codes
+        bg[m] = ((const uint16_t*)gsrow)[cc[m] >> 1] | (uint32_t)((const uint16_t*)gbrow)[cc[m] >> 1] << 16;
+        bu[m] = ((const uint16_t*)usrow)[cc[m] >> 1] | (uint32_t)((const uint16_t*)ubrow)[cc[m] >> 1] << 16;
       }
     }
     // keep every weight load of the slice ahead of the arithmetic: left to itself the
@@ -219,10 +275,21 @@ __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* u
         sg = okf[m] != 0.f ? e8m0_to_f32(bg[m]) : 0.f;
         su = okf[m] != 0.f ? e8m0_to_f32(bu[m]) : 0.f;
       }
+      float cg = 0.f, cu = 0.f;
+      if constexpr (WT == MOE_INT4G64) {
+        const float s_g = bf16lo(bg[m]), s_u = bf16lo(bu[m]);
+        sg = okf[m] != 0.f ? s_g : 0.f;
+        su = okf[m] != 0.f ? s_u : 0.f;
+        cg = okf[m] != 0.f ? fmaf(-128.f, s_g, bf16hi(bg[m])) : 0.f;
+        cu = okf[m] != 0.f ? fmaf(-128.f, s_u, bf16hi(bu[m])) : 0.f;
+      }
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
         if (!((mask >> t) & 1u)) continue;  // uniform
-        C::dot(dg, du, xb + (size_t)t * xstride, cc[m], sg, su, ag[t], au[t]);
+        if constexpr (WT == MOE_INT4G64)
+          C::dot(dg, du, xb + (size_t)t * xstride, cc[m], sg, cg, su, cu, ag[t], au[t]);
+        else
+          C::dot(dg, du, xb + (size_t)t * xstride, cc[m], sg, su, ag[t], au[t]);
       }
     }
   }
@@ -305,6 +372,34 @@ template <> struct DN<MOE_MXFP4> {
   }
 };
 
+// Group-wise affine 4-bit: 32 codes (half a group of 64) per chunk, each weight s * q + b with
+// the group's bf16 scale and bias, formed in fp32 (exact: a bf16 scale times a 4-bit integer has
+// 12 significant bits) and multiplied by the fp32 activation.
+template <> struct DN<MOE_INT4G64> {
+  static constexpr int EPC = 32;
+  typedef uint4 W;
+  static __device__ __forceinline__ W load(const uint8_t* row, int c) { return ldg16(row + (size_t)c * 16); }
+  // elements 8j .. 8j + 7: codes of even elements in the bytes of q & 0x0F0F0F0F, odd ones in
+  // the bytes of (q >> 4) & 0x0F0F0F0F
+  static __device__ __forceinline__ float dword_dot(uint32_t q, float4 x0, float4 x1, float s, float b, float acc) {
+    const uint32_t ev = q & 0x0F0F0F0Fu, od = (q >> 4) & 0x0F0F0F0Fu;
+    const float xe[4] = {x0.x, x0.z, x1.x, x1.z}, xo[4] = {x0.y, x0.w, x1.y, x1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(fmaf(s, (float)((ev >> (8 * i)) & 0xFFu), b), xe[i], acc);
+      acc = fmaf(fmaf(s, (float)((od >> (8 * i)) & 0xFFu), b), xo[i], acc);
+    }
+    return acc;
+  }
+  static __device__ __forceinline__ float dot_affine(W w, const float* a, int c, float s, float b) {
+    const float* p = a + (size_t)c * 32;
+    float acc = dword_dot(w.x, ldf4(p), ldf4(p + 4), s, b, 0.f);
+    acc = dword_dot(w.y, ldf4(p + 8), ldf4(p + 12), s, b, acc);
+    acc = dword_dot(w.z, ldf4(p + 16), ldf4(p + 20), s, b, acc);
+    return dword_dot(w.w, ldf4(p + 24), ldf4(p + 28), s, b, acc);
+  }
+};
+
 template <int WT>
 __device__ __forceinline__ size_t row_bytes(int K) {
   return WT == MOE_F32 ? (size_t)K * 4 : WT == MOE_BF16 ? (size_t)K * 2 : (size_t)K / 2;
@@ -323,12 +418,11 @@ constexpr int kWaves = kThreads / kWave;
 // x chunks of a pass are loaded into registers before any is used (loads consumed as they
 // are issued would wait one L2 round trip each).
 template <int XT, int TM>
-__global__ __launch_bounds__(kThreads) void dec_router(Args A) {
+__device__ __forceinline__ void router_block(const Args& A, int e) {
   constexpr int RC = TM <= 4 ? 4 : TM <= 8 ? 2 : 1;  // 16-byte weight chunks per lane per pass
   typedef typename std::conditional<XT == MOE_F32, float4, uint2>::type XV;
   __shared__ float s_p[kWaves][TM];
   const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int e = blockIdx.x;
   if (A.logits_in) {  // routing on given logits: copy them, no router
     for (int t = threadIdx.x; t < A.T; t += blockDim.x) {
       const float l = A.logits_in[(size_t)t * A.E + e];
@@ -403,6 +497,11 @@ __global__ __launch_bounds__(kThreads) void dec_router(Args A) {
   }
 }
 
+template <int XT, int TM>
+__global__ __launch_bounds__(kThreads) void dec_router(Args A) {
+  router_block<XT, TM>(A, blockIdx.x);
+}
+
 // The shared expert's gate/up + SwiGLU for every token: one wave per shared row (the 64 lanes
 // split K = H, kShNch chunks each per pass), a_sh[t][row] = silu(g) * u.  It needs no routing,
 // so it runs in the blocks of a kernel that would otherwise leave HBM idle while it selects
@@ -423,8 +522,8 @@ __device__ __forceinline__ void shared_gateup_block(const Args& A, int blk, int 
   const unsigned mask = (A.T >= 32) ? 0xffffffffu : ((1u << A.T) - 1u);
   const size_t xstride = (size_t)A.H * XS<XT>::BYTES;
   gateup_row<XT, SWT, kWave, kShNch, TM, XL>((const uint8_t*)A.sgate + r * rb,
-                                             (const uint8_t*)A.sup + r * rb, nullptr, nullptr,
-                                             A.H / GU<SWT>::EPC, (const uint8_t*)A.x, s_x,
+                                             (const uint8_t*)A.sup + r * rb, nullptr, nullptr, nullptr,
+                                             nullptr, A.H / GU<SWT>::EPC, (const uint8_t*)A.x, s_x,
                                              (int)(A.T * xstride), xstride, mask, slots, A.a_sh,
                                              A.Is, row, lane, valid);
 }
@@ -598,14 +697,19 @@ __global__ __launch_bounds__(kThreads) void dec_gateup(Args A, int tiles, int sh
   const bool valid = row < A.I;
   const size_t r = (size_t)e * A.I + (valid ? row : 0);
   const size_t rb = row_bytes<WT>(A.H);
-  const uint8_t *gsr = nullptr, *usr = nullptr;
+  const void *gsr = nullptr, *usr = nullptr, *gbr = nullptr, *ubr = nullptr;
   if constexpr (WT == MOE_MXFP4) {
-    gsr = A.gs + r * (A.H / 32);
-    usr = A.us + r * (A.H / 32);
+    gsr = (const uint8_t*)A.gs + r * (A.H / 32);
+    usr = (const uint8_t*)A.us + r * (A.H / 32);
+  } else if constexpr (WT == MOE_INT4G64) {
+    gsr = (const uint16_t*)A.gs + r * (A.H / 64);
+    usr = (const uint16_t*)A.us + r * (A.H / 64);
+    gbr = (const uint16_t*)A.gb + r * (A.H / 64);
+    ubr = (const uint16_t*)A.ub + r * (A.H / 64);
   }
   const size_t xstride = (size_t)A.H * XS<XT>::BYTES;
   gateup_row<XT, WT, G, NCH, TM, XL>((const uint8_t*)A.gate + r * rb, (const uint8_t*)A.up + r * rb,
-                                     gsr, usr, A.H / GU<WT>::EPC, (const uint8_t*)A.x, s_x,
+                                     gsr, usr, gbr, ubr, A.H / GU<WT>::EPC, (const uint8_t*)A.x, s_x,
                                      (int)(T * xstride), xstride, mask, slots, A.a, A.I, row, gl,
                                      valid);
 }
@@ -668,7 +772,8 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
       for (int m = 0; m < NCH; ++m) {
         const int c = sl * G * NCH + gl + G * m;
         bf.w[m] = DN<SWT>::load(row, c < nchs ? c : 0);
-        if constexpr (WT == MOE_MXFP4) bf.sb[m] = 127u;  // unit scale (never used for shared rows)
+        if constexpr (WT == MOE_MXFP4) bf.sb[m] = 127u;     // unit scale (never used for shared rows)
+        if constexpr (WT == MOE_INT4G64) bf.sb[m] = 0x3F80u;  // scale 1, bias 0 (never used either)
       }
       return;
     }
@@ -683,7 +788,11 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
       const int c = sl * G * NCH + gl + G * m;
       const int cc = c < nch ? c : 0;
       bf.w[m] = DN<WT>::load(row, cc);
-      if constexpr (WT == MOE_MXFP4) bf.sb[m] = A.ds[((size_t)e * A.H + hh) * (A.I / 32) + cc];
+      if constexpr (WT == MOE_MXFP4) bf.sb[m] = ((const uint8_t*)A.ds)[((size_t)e * A.H + hh) * (A.I / 32) + cc];
+      if constexpr (WT == MOE_INT4G64) {  // bf16 bias << 16 | bf16 scale of the chunk's group
+        const size_t gi = ((size_t)e * A.H + hh) * (A.I / 64) + (cc >> 1);
+        bf.sb[m] = ((const uint16_t*)A.ds)[gi] | (uint32_t)((const uint16_t*)A.db)[gi] << 16;
+      }
     }
   };
   auto flush = [&]() {
@@ -744,6 +853,9 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
         float d;
         if constexpr (WT == SWT)
           d = DN<WT>::dot(bf.w[m], arow, cc[m]);
+        else if constexpr (WT == MOE_INT4G64)
+          d = sh ? DN<SWT>::dot(bf.w[m], arow, cc[m])
+                 : DN<WT>::dot_affine(bf.w[m], arow, cc[m], bf16lo(bf.sb[m]), bf16hi(bf.sb[m]));
         else
           d = sh ? DN<SWT>::dot(bf.w[m], arow, cc[m]) : DN<WT>::dot(bf.w[m], arow, cc[m]);
         part = fmaf(sc[m], d, part);
@@ -752,29 +864,66 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
     }
   };
 
+  // Prologue.  The plan words and the first pass of activations are loaded into registers
+  // first; then, when this wave's first item belongs to the shared expert (its weights need no
+  // plan), that item's weight loads are issued; only then is the staged data stored to LDS.
+  // Loads complete in issue order, so the stores wait for the staging loads alone and the
+  // shared weights are in flight across the staging barrier.
+  const int tid = threadIdx.x, bd = blockDim.x;
+  constexpr int kPl = 4;  // plan cells per thread: D * T <= 16 * 16 * 16 = 4096 with 1024 threads
+  constexpr int kStg = 4;  // activation float4 per thread in the first staging pass
+  int r_e = 0, r_sl[kPl];
+  unsigned r_m = 0;
+  float r_w[kPl];
+  if (tid < D) {
+    r_e = P.dexp()[tid];
+    r_m = P.dmask()[tid];
+  }
+#pragma unroll
+  for (int j = 0; j < kPl; ++j) {
+    const int i = tid + j * bd;
+    r_sl[j] = i < D * T ? P.dslot()[i] : 0;
+    r_w[j] = i < D * T ? P.dw()[i] : 0.f;
+  }
+  const int n4 = ALDS ? S * A.I / 4 : 0, n4s = ALDS ? T * A.Is / 4 : 0;
+  float4 sv[kStg];
+#pragma unroll
+  for (int j = 0; j < kStg; ++j) {
+    const int i = tid + j * bd;
+    if (i < n4 + n4s) sv[j] = i < n4 ? ldf4(A.a + (size_t)i * 4) : ldf4(A.a_sh + (size_t)(i - n4) * 4);
+  }
+  Buf a, b;
+  const bool early = wave < nqs;  // uniform: the first item is a shared one
+  if (early) load(wave, a);
+  if (tid < D) {
+    s_e[tid] = r_e;
+    s_m[tid] = r_m;
+  }
+#pragma unroll
+  for (int j = 0; j < kPl; ++j) {
+    const int i = tid + j * bd;
+    if (i < D * T) {
+      s_sl[i] = r_sl[j];
+      s_w[i] = r_w[j];
+    }
+  }
+  for (int i = tid; i < nrgb_max * NW * TM * RB; i += bd) s_part[i] = 0.f;
+  // staging unit i: routed activations [S][I] for i < n4, then the shared ones [T][I_s]
+  auto stage_dst = [&](int i) { return i < n4 ? (float4*)s_act + i : (float4*)s_ash + (i - n4); };
+#pragma unroll
+  for (int j = 0; j < kStg; ++j) {
+    const int i = tid + j * bd;
+    if (i < n4 + n4s) *stage_dst(i) = sv[j];
+  }
+  for (int i = tid + kStg * bd; i < n4 + n4s; i += bd)  // larger windows: the rest, pass by pass
+    *stage_dst(i) = i < n4 ? ldf4(A.a + (size_t)i * 4) : ldf4(A.a_sh + (size_t)(i - n4) * 4);
   nd = *P.nd();
-  for (int i = threadIdx.x; i < D; i += blockDim.x) {
-    s_e[i] = P.dexp()[i];
-    s_m[i] = P.dmask()[i];
-  }
-  for (int i = threadIdx.x; i < D * T; i += blockDim.x) {
-    s_sl[i] = P.dslot()[i];
-    s_w[i] = P.dw()[i];
-  }
-  for (int i = threadIdx.x; i < nrgb_max * NW * TM * RB; i += blockDim.x) s_part[i] = 0.f;
-  if constexpr (ALDS) {
-    const int n4 = S * A.I / 4;
-    for (int i = threadIdx.x; i < n4; i += blockDim.x) ((float4*)s_act)[i] = ldf4(A.a + (size_t)i * 4);
-    const int n4s = T * A.Is / 4;
-    for (int i = threadIdx.x; i < n4s; i += blockDim.x) ((float4*)s_ash)[i] = ldf4(A.a_sh + (size_t)i * 4);
-  }
   __syncthreads();
   per_rg = nsl * nd;
   const int nq = nqs + nrgb * per_rg;
   const int nmine = wave < nq ? (nq - 1 - wave) / NW + 1 : 0;
   if (nmine > 0) {  // uniform; this wave's items are q = wave + NW * step
-    Buf a, b;
-    load(wave, a);
+    if (!early) load(wave, a);
     stream_loaded<Buf>(nmine, a, b, [&](int st, Buf& bf) { load(wave + NW * st, bf); },
                        [&](int st, const Buf& bf) { consume(wave + NW * st, bf); });
     flush();
@@ -908,7 +1057,7 @@ void* down_fn(int gi) {
   return nullptr;
 }
 
-int gu_epc(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : 32; }
+int gu_epc(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : 32; }  // MXFP4, INT4G64: 32
 int dn_epc(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : 32; }
 constexpr int kMaxLdsX = 64 * 1024;  // x staged in LDS by the gate/up kernels up to this size
 
@@ -917,11 +1066,6 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   constexpr const GN* GUL = TM == 1 ? kGU1 : kGUn;
   const DevInfo dv = dev_info();
   const int S = A.T * A.k, D = S < A.E ? S : A.E;
-  void* args1[] = {&A};
-  hipError_t err = launch(hook, "dec_router", router_fn<XT>(A.T), dim3(A.E), dim3(kThreads), args1, 0, st);
-  if (err != hipSuccess) return MOE_EHIP;
-  if (route_only) return MOE_OK;
-
   // x goes through LDS (its loads issued ahead of the weights, read back at LDS latency); one
   // token's row always fits (H <= MOE_MAX_H fp32 values are 64 KiB)
   const size_t xbytes = (size_t)A.T * A.H * (XT == MOE_F32 ? 4 : 2);
@@ -931,6 +1075,10 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   // routed rows of the gate/up kernel (T = 1)
   const int sh_waves = TM == 1 ? kWaves : TM;
   int nsh = A.Is > 0 ? (A.Is + sh_waves - 1) / sh_waves : 0;
+  void* args1[] = {&A};
+  hipError_t err = launch(hook, "dec_router", router_fn<XT>(A.T), dim3(A.E), dim3(kThreads), args1, 0, st);
+  if (err != hipSuccess) return MOE_EHIP;
+  if (route_only) return MOE_OK;
   if (TM > 1) {
     void* fs = xl ? (void*)dec_select<XT, SWT, TM, true> : (void*)dec_select<XT, SWT, TM, false>;
     void* args_s[] = {&A, &nsh};

@@ -1,5 +1,5 @@
 // Decode path instantiation unit: compiled once per (dtype combination, token tile) with
-//   -DMOE_DEC_NAME=<f32|bf16|fp4> -DMOE_DEC_TM=<1|4|8|16>
+//   -DMOE_DEC_NAME=<f32|bf16|fp4|i4> -DMOE_DEC_TM=<1|4|8|16>
 // so that the kernels of decode_impl.h build in parallel units.
 #include "decode_impl.h"
 
@@ -16,9 +16,11 @@ namespace {
 constexpr int kDecF32[3] = {MOE_F32, MOE_F32, MOE_F32};
 constexpr int kDecBf16[3] = {MOE_BF16, MOE_BF16, MOE_BF16};
 constexpr int kDecFp4[3] = {MOE_BF16, MOE_MXFP4, MOE_BF16};
+constexpr int kDecI4[3] = {MOE_BF16, MOE_INT4G64, MOE_BF16};
 #define MOE_DT_f32 kDecF32
 #define MOE_DT_bf16 kDecBf16
 #define MOE_DT_fp4 kDecFp4
+#define MOE_DT_i4 kDecI4
 #define MOE_DT2(n) MOE_DT_##n
 #define MOE_DT(n) MOE_DT2(n)
 }  // namespace

@@ -16,7 +16,7 @@
 //           epilogue, one bf16 row per slot.
 //  combine  y[t] = sum_j out[t*k + j] + out_shared[t], a fixed order (deterministic).
 //
-// MXFP4 experts take the precise variant (template flag P) of the same kernels: the gate/up
+// MXFP4 and group-wise affine 4-bit experts take the precise variant (template flag P) of the same kernels: the gate/up
 // epilogue stores each fp32 activation as two bf16 parts, hi = bf16(a) and lo = bf16(a - hi),
 // the down GEMM multiplies both parts by the same weight fragment (two MFMAs accumulating in
 // fp32, so the activations keep about 16 significant bits instead of 8), and the per-slot rows
@@ -105,7 +105,7 @@ PfLayout pf_layout(const Args& A) {
   b += up(sizeof(int) * 4 * (size_t)prefill_tiles_cap(A.T, A.E, A.k));
   L.ntiles = (int*)b;
   b += up(256);
-  const bool precise = A.wdt == MOE_MXFP4;
+  const bool precise = A.wdt == MOE_MXFP4 || A.wdt == MOE_INT4G64;
   L.act = (uint16_t*)b;
   b += up(2 * R * Imax);
   L.act_lo = nullptr;
@@ -244,7 +244,8 @@ __device__ __forceinline__ void wait_vm() {
 // LDS sizes of one pf_gemm instance (16-byte units); the host sizes dynamic LDS from them.
 template <int MODE, int BM, int NS, int WT, bool P>
 struct PfCfg {
-  static constexpr bool F4 = WT == MOE_MXFP4;
+  static constexpr bool F4 = WT == MOE_MXFP4 || WT == MOE_INT4G64;  // 4-bit codes, 16 bytes per row per step
+  static constexpr bool I4 = WT == MOE_INT4G64;                     // + a bf16 bias block per wave
   static constexpr bool AHL = P && MODE == 1;                    // A = activation hi and lo parts
   static constexpr int kUnitsA = BM * kPfBK * 2 / 16;             // one A part per stage
   static constexpr int kStageA = kUnitsA * (AHL ? 2 : 1);
@@ -259,7 +260,7 @@ template <int MODE, int BM, int NS, int WT, bool P>
 __global__ __launch_bounds__(2 * BM, BM == 128 ? (NS == 2 ? 3 : 2) : 1)
 void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
   typedef PfCfg<MODE, BM, NS, WT, P> C;
-  constexpr bool F4 = C::F4;
+  constexpr bool F4 = C::F4, I4 = C::I4;
   constexpr int kStageA = C::kStageA, kStage = C::kStage, kNA = C::kNA, kNB = C::kNB;
   extern __shared__ __attribute__((aligned(16))) uint4 smem_dyn[];
   __shared__ __attribute__((aligned(16))) uint4 smem_st[C::kDyn ? 1 : NS * kStage];
@@ -327,12 +328,13 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
     }
     ao[j] = rowb == kOOB ? kOOB : rowb + c * 16u;
   }
-  // MXFP4 B: row r of the tile is lane r % 64 of wave r / 64, one 16-byte chunk (32 codes) per
-  // step.  The e8m0 scales (sb = K / 32 bytes per row) of a wave's 64 rows are one contiguous
-  // block of the scale matrix, 16-byte aligned (64 sb is a multiple of 16), staged in LDS for
-  // the whole tile at wstr bytes per wave.
-  const int sb = F4 ? K / 32 : 0, sbi = (64 * sb + 1023) / 1024, wstr = sbi * 1024;
-  i32x4_t rs;
+  // 4-bit B: row r of the tile is lane r % 64 of wave r / 64, one 16-byte chunk (32 codes) per
+  // step.  The scales of a wave's 64 rows -- MXFP4: one e8m0 byte per 32; INT4G64: one bf16 per
+  // 64, so sb = K / 32 bytes per row either way -- are one contiguous, 16-byte aligned block of
+  // the scale matrix (64 sb is a multiple of 16), staged in LDS for the whole tile at wstr bytes
+  // per wave; INT4G64 stages the bias block of the same rows right after it (wtot bytes per wave).
+  const int sb = F4 ? K / 32 : 0, sbi = (64 * sb + 1023) / 1024, wstr = sbi * 1024, wtot = (I4 ? 2 : 1) * wstr;
+  i32x4_t rs, rbi;
   uint32_t so = kOOB;  // the wave's first scale row's offset (uniform)
 #pragma unroll
   for (int j = 0; j < kNB; ++j) {
@@ -357,7 +359,9 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
         const uint8_t* base = (const uint8_t*)(up ? A.up : A.gate) + (size_t)g * A.I * (A.H / 2);
         rb[j] = buf_rsrc(base, (size_t)N * (A.H / 2));
         if (col < N) rowb = (uint32_t)col * (A.H / 2);
-        rs = buf_rsrc((up ? A.us : A.gs) + (size_t)g * A.I * (A.H / 32), (size_t)N * (A.H / 32));
+        rs = buf_rsrc((const uint8_t*)(up ? A.us : A.gs) + (size_t)g * A.I * (A.H / 32), (size_t)N * (A.H / 32));
+        if constexpr (I4)
+          rbi = buf_rsrc((const uint8_t*)(up ? A.ub : A.gb) + (size_t)g * A.I * (A.H / 32), (size_t)N * (A.H / 32));
         so = (uint32_t)(n0 + half * 64) * (A.H / 32);
       } else {
         const uint16_t* base = up ? (sh ? (const uint16_t*)A.sup : (const uint16_t*)A.up + (size_t)g * A.I * A.H)
@@ -370,7 +374,8 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
       if constexpr (F4) {
         rb[j] = buf_rsrc((const uint8_t*)A.down + (size_t)g * A.H * (A.I / 2), (size_t)A.H * (K / 2));
         if (h < A.H) rowb = (uint32_t)h * (K / 2);
-        rs = buf_rsrc(A.ds + (size_t)g * A.H * (A.I / 32), (size_t)A.H * (K / 32));
+        rs = buf_rsrc((const uint8_t*)A.ds + (size_t)g * A.H * (A.I / 32), (size_t)A.H * (K / 32));
+        if constexpr (I4) rbi = buf_rsrc((const uint8_t*)A.db + (size_t)g * A.H * (A.I / 32), (size_t)A.H * (K / 32));
         so = (uint32_t)(n0 + wave * 64) * (K / 32);
       } else {
         const uint16_t* base = g == A.E ? (const uint16_t*)A.sdown : (const uint16_t*)A.down + (size_t)g * A.H * A.I;
@@ -406,7 +411,11 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
   uint8_t* s_sc = (uint8_t*)(smem + NS * kStage);
   if constexpr (F4) {
     for (int i = 0; i < sbi; ++i)
-      dma16(rs, so + (uint32_t)(i * 64 + lane) * 16u, lds_addr((uint4*)(s_sc + (size_t)wave * wstr) + i * 64));
+      dma16(rs, so + (uint32_t)(i * 64 + lane) * 16u, lds_addr((uint4*)(s_sc + (size_t)wave * wtot) + i * 64));
+    if constexpr (I4)
+      for (int i = 0; i < sbi; ++i)
+        dma16(rbi, so + (uint32_t)(i * 64 + lane) * 16u,
+              lds_addr((uint4*)(s_sc + (size_t)wave * wtot + wstr) + i * 64));
   }
 
   // down: the tile's slots and routing weights, staged in LDS while the operands stream
@@ -447,9 +456,23 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int br = wn * 128 + n * 32 + (lane & 31);
-        if constexpr (F4) {  // 8 codes of this lane's K range, scaled while unpacked to bf16
+        if constexpr (I4) {  // 8 codes -> bf16(s * q + b), the group's scale and bias (one group per 2 steps)
           const uint32_t q = ((const uint32_t*)(st + kStageA + br))[c];
-          const float sc = e8m0_to_f32(s_sc[(br >> 6) * wstr + (br & 63) * sb + s0 + s]);
+          const uint8_t* sp = s_sc + (br >> 6) * wtot + (br & 63) * sb + 2 * ((s0 + s) >> 1);
+          const float gs = bf16_to_f32(*(const uint16_t*)sp), gb = bf16_to_f32(*(const uint16_t*)(sp + wstr));
+          const uint32_t ev = q & 0x0F0F0F0Fu, od = (q >> 4) & 0x0F0F0F0Fu;
+          uint32_t v[4];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            typedef float f2 __attribute__((ext_vector_type(2)));
+            typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+            const f2 w2 = {fmaf(gs, (float)((ev >> (8 * p)) & 0xFFu), gb), fmaf(gs, (float)((od >> (8 * p)) & 0xFFu), gb)};
+            v[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, b2));
+          }
+          bfr[n] = __builtin_bit_cast(bf16x8_t, make_uint4(v[0], v[1], v[2], v[3]));
+        } else if constexpr (F4) {  // 8 codes of this lane's K range, scaled while unpacked to bf16
+          const uint32_t q = ((const uint32_t*)(st + kStageA + br))[c];
+          const float sc = e8m0_to_f32(s_sc[(br >> 6) * wtot + (br & 63) * sb + s0 + s]);
           uint32_t v[4];
           v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 0));
           v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1));
@@ -678,7 +701,7 @@ template <int MODE, int NS, int WT, bool P>
 size_t pf_lds(int K) {
   typedef PfCfg<MODE, kPfBM, NS, WT, P> C;
   if (!C::kDyn) return 0;
-  const size_t sc = C::F4 ? (size_t)4 * ((64 * (K / 32) + 1023) / 1024) * 1024 : 0;
+  const size_t sc = C::F4 ? (size_t)(C::I4 ? 2 : 1) * 4 * ((64 * (K / 32) + 1023) / 1024) * 1024 : 0;
   const size_t epi = (MODE == 1 && P) ? 0 : (size_t)kPfBM * ((MODE == 0 ? kPfBN / 2 : kPfBN) + 8) * 2;
   return std::max(C::ring_bytes + sc, epi);
 }
@@ -693,9 +716,13 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   if (rc) return rc;
   const int cap = prefill_tiles_cap(A.T, A.E, A.k);
   const int Imax = A.I > A.Is ? A.I : A.Is;
-  const bool f4 = A.wdt == MOE_MXFP4;
+  const bool f4 = A.wdt == MOE_MXFP4, i4 = A.wdt == MOE_INT4G64;
   // MXFP4 experts: the routed groups' tiles run the MXFP4 kernel, the shared expert's tiles the
-  // bf16 kernel, both in the precise variant (activation hi + lo parts, fp32 slot rows)
+  // bf16 kernel, both in the precise variant (activation hi + lo parts, fp32 slot rows).
+  // INT4G64 experts: the routed tiles run the int4 kernel (weights rebuilt in bf16 on the way
+  // into the MFMA), the shared tiles the bf16 kernel, both precise as for MXFP4.  The weights'
+  // own bf16 rounding stays (the page's reconstruction); the activations and slot rows keep
+  // about 16 significant bits, so those roundings do not add to it.
   auto run = [&](const char* name, const void* f, int nblocks, int nbt, int part, size_t lds) -> int {
     PfLayout Lc = L;
     void* args[] = {&A, &Lc, &nbt, &nblocks, &part};
@@ -704,7 +731,13 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   const int shtiles = A.Is > 0 ? (A.T + kPfBM - 1) / kPfBM : 0;
   {
     const int nbt = (Imax + kPfBN / 2 - 1) / (kPfBN / 2);
-    if (!f4) {
+    if (i4) {
+      rc = run("pf_gateup", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_INT4G64, true>, cap * nbt, nbt, 1,
+               pf_lds<0, kPfNS, MOE_INT4G64, true>(A.H));
+      if (!rc && shtiles)
+        rc = run("pf_gateup_shared", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, true>, shtiles * nbt, nbt, 2,
+                 pf_lds<0, kPfNS, MOE_BF16, true>(A.H));
+    } else if (!f4) {
       rc = run("pf_gateup", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, false>, cap * nbt, nbt, 0, 0);
     } else {
       rc = run("pf_gateup", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_MXFP4, true>, cap * nbt, nbt, 1,
@@ -717,7 +750,13 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   }
   {
     const int nbt = (A.H + kPfBN - 1) / kPfBN;
-    if (!f4) {
+    if (i4) {
+      rc = run("pf_down", (const void*)pf_gemm<1, kPfBM, kPfNS, MOE_INT4G64, true>, cap * nbt, nbt, 1,
+               pf_lds<1, kPfNS, MOE_INT4G64, true>(A.I));
+      if (!rc && shtiles)
+        rc = run("pf_down_shared", (const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, true>, shtiles * nbt, nbt, 2,
+                 pf_lds<1, kPfNSG, MOE_BF16, true>(A.Is));
+    } else if (!f4) {
       rc = run("pf_down", (const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, false>, cap * nbt, nbt, 0, 0);
     } else {
       rc = run("pf_down", (const void*)pf_gemm<1, kPfBM, kPfNS, MOE_MXFP4, true>, cap * nbt, nbt, 1,

@@ -35,6 +35,12 @@ def workload_spec(name, T_override=None, d=32):
     if name == "qwen_prefill":
         return dict(T=T_override or 4096, H=2048, E=256, k=8, I=512, I_shared=512, act="bf16", expert="bf16",
                     shared="bf16", out="bf16", bias="zipf", d=None, layers=8)
+    if name == "qwen_int4":   # the Qwen checkpoint's group-wise affine 4-bit experts
+        return dict(T=T_override or 1, H=2048, E=256, k=8, I=512, I_shared=512, act="bf16", expert="int4g64",
+                    shared="bf16", out="bf16", bias=None, d=None, layers=48)
+    if name == "qwen_int4_prefill":
+        return dict(T=T_override or 4096, H=2048, E=256, k=8, I=512, I_shared=512, act="bf16", expert="int4g64",
+                    shared="bf16", out="bf16", bias="zipf", d=None, layers=8)
     if name == "tiny":
         return dict(T=T_override or 4, H=256, E=16, k=2, I=128, I_shared=128, act="f32", expert="f32",
                     shared="f32", out="f32", bias=None, d=None, layers=1)
@@ -48,8 +54,10 @@ def _es(dt):
 def expert_bytes(spec):
     """Bytes of one routed expert's gate+up and of its down weights."""
     H, I = spec["H"], spec["I"]
-    if spec["expert"] == "mxfp4":
+    if spec["expert"] == "mxfp4":     # codes + one e8m0 byte per 32
         return 2 * (I * H // 2 + I * H // 32), H * I // 2 + H * I // 32
+    if spec["expert"] == "int4g64":   # codes + a bf16 scale and a bf16 bias per 64
+        return 2 * (I * H // 2 + I * H // 16), H * I // 2 + H * I // 16
     es = _es(spec["expert"])
     return 2 * I * H * es, H * I * es
 
@@ -77,9 +85,9 @@ def kernel_work(spec, distinct):
     ss, xs, ys = _es(spec["shared"]), _es(spec["act"]), _es(spec["out"])
     sh_gu, sh_dn = 2 * Is * H * ss, Is * H * ss
     S = T * k                                  # routed rows (slots); the shared expert adds T rows
-    # MXFP4 prefill runs the precise kernels: activations as bf16 hi + lo (4 B per value), fp32
+    # MXFP4 and int4 prefill run the precise kernels: activations as bf16 hi + lo (4 B per value), fp32
     # slot rows, and the shared expert's tiles in launches of their own
-    p = spec["expert"] == "mxfp4"
+    p = spec["expert"] in ("mxfp4", "int4g64")
     ab, rb = (4, 4) if p else (2, 2)           # bytes per activation value, per slot-row value
     w = {
         # decode (T <= 16)

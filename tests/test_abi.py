@@ -65,6 +65,9 @@ def test_strerror_covers_codes(lib):
     # MXFP4 on the grouped-GEMM path: a tile's scale rows must fit in LDS (H, I <= 8192)
     (dict(T=64, expert_dtype=2, H=8224), B.MOE_EUNSUPPORTED),
     (dict(T=64, expert_dtype=2, I=8192 + 32), B.MOE_EUNSUPPORTED),
+    # group-wise affine 4-bit: groups of 64 along H and I
+    (dict(expert_dtype=3, H=2048 + 32), B.MOE_EUNSUPPORTED), (dict(expert_dtype=3, I=512 + 32), B.MOE_EUNSUPPORTED),
+    (dict(expert_dtype=3, act_dtype=0, shared_dtype=0), B.MOE_EUNSUPPORTED),
 ])
 def test_shape_validation(lib, kw, code):
     rc, _ = _ws(_shape(**kw))
@@ -78,6 +81,7 @@ def test_workspace_sizes_and_paths(lib):
                      (dict(T=17), "prefill.bf16"), (dict(T=4096), "prefill.bf16"),
                      (dict(T=4096, H=2560, E=512, I=768, I_shared=768, expert_dtype=2, out_dtype=0),
                       "prefill.mxfp4"), (dict(T=64, expert_dtype=2, H=8192), "prefill.mxfp4"),
+                     (dict(expert_dtype=3), "decode.int4g64"), (dict(T=4096, expert_dtype=3), "prefill.int4g64"),
                      (dict(T=4, H=256, E=16, k=2, I=128, I_shared=128, act_dtype=0, expert_dtype=0,
                            shared_dtype=0, out_dtype=0), "decode.f32")]:
         s = _shape(**kw)
@@ -111,6 +115,13 @@ def test_forward_argument_errors_enqueue_nothing(lib):
     # MXFP4 needs its scale arrays, 16-byte aligned
     assert _call_forward(_shape(expert_dtype=2), w=good) == B.MOE_EINVAL
     w = B.Weights.from_buffer_copy(good); w.gate_s, w.up_s, w.down_s = 0x90000, 0xA0000, 0xB0000
+    # group-wise affine 4-bit needs scales and biases, 16-byte aligned
+    assert _call_forward(_shape(expert_dtype=3), w=w) == B.MOE_EINVAL
+    w4 = B.Weights.from_buffer_copy(w); w4.gate_b, w4.up_b, w4.down_b = 0xC0000, 0xD0000, 0xE0000
+    assert _call_forward(_shape(expert_dtype=3), w=w4, ws=None) == B.MOE_EWORKSPACE
+    for f in ("gate_b", "up_b", "down_b", "down_s"):
+        wm = B.Weights.from_buffer_copy(w4); setattr(wm, f, getattr(w4, f) + 2)
+        assert _call_forward(_shape(expert_dtype=3), w=wm) == B.MOE_EALIGN, f
     rc, need = _ws(_shape(expert_dtype=2, out_dtype=0))
     assert _call_forward(_shape(expert_dtype=2, out_dtype=0), w=w, ws=None) == B.MOE_EWORKSPACE
     for f in ("gate_s", "up_s", "down_s"):

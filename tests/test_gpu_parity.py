@@ -14,6 +14,12 @@ Bars (floating point compared with the oracle's double-precision result):
     relative L2 <= 5e-3;
   * MXFP4 experts with fp32 output: relative L2 <= 1e-3 on both paths (the grouped GEMMs
     carry the activations as bf16 hi + lo parts and the slot rows in fp32);
+  * group-wise affine 4-bit experts (int4g64): relative L2 <= 1e-3 on the decode path with an
+    fp32 output (each weight s*q + b is formed exactly in fp32), the bf16 bars with a bf16 output;
+    on the grouped-GEMM path relative L2 <= 5e-3 and max relative error <= 3e-2: the GEMM rebuilds
+    each weight in bf16 before its multiply, as the page's kernel does, one more rounding of up to
+    2^-9 in each of the two GEMMs than a bf16 layer has (expected relative L2 about 3e-3; the
+    largest of 8M elements near 6 standard deviations of that, about 1.8e-2);
   * all-fp32 layer: relative L2 <= 1e-5 (fp32 accumulation over <= 2^12 terms stays
     near 1e-6).
 """
@@ -72,6 +78,12 @@ def check_out(L, y, ref, tag):
     if L.expert_dtype == "mxfp4":
         assert L.out_dtype == "f32", "the MXFP4 bar is stated on an fp32 output"
         assert l2 <= 1e-3, tag
+    elif L.expert_dtype == "int4g64" and L.T <= 16 and L.out_dtype == "f32":
+        assert l2 <= 1e-3, tag
+    elif L.expert_dtype == "int4g64" and L.T <= 16:
+        assert max_rel <= 2e-2 and l2 <= 5e-3, tag
+    elif L.expert_dtype == "int4g64":
+        assert max_rel <= 3e-2 and l2 <= 5e-3, tag
     elif L.out_dtype == "bf16":
         assert max_rel <= 2e-2 and l2 <= 5e-3, tag
     elif L.act_dtype == "f32" and L.expert_dtype == "f32":
@@ -88,8 +100,8 @@ def host_view_for_oracle(Ld, xd, ids_needed=None):
     def cp(t):
         return None if t is None else t.cpu().numpy()
     Lh = synth.to_host(dataclasses.replace(Ld, gate=None, up=None, down=None, gate_s=None, up_s=None,
-                                           down_s=None))
-    for f in ("gate", "up", "down", "gate_s", "up_s", "down_s"):
+                                           down_s=None, gate_b=None, up_b=None, down_b=None))
+    for f in ("gate", "up", "down", "gate_s", "up_s", "down_s", "gate_b", "up_b", "down_b"):
         t = getattr(Ld, f)
         if t is None:
             continue
@@ -189,7 +201,8 @@ def full_check(orc, B, Lh, xh, Ld, xd, tag, copy_selected=False):
     import torch
     if Lh is None:
         Lh, xh = host_view_for_oracle(dataclasses.replace(Ld, gate=None, up=None, down=None, gate_s=None,
-                                                          up_s=None, down_s=None), xd)
+                                                          up_s=None, down_s=None, gate_b=None, up_b=None,
+                                                          down_b=None), xd)
     lg, ids, w = oracle_routing(orc, Lh, xh)
     if copy_selected:
         Lh, xh = host_view_for_oracle(Ld, xd, ids_needed=candidate_experts(orc, lg, ids, Lh.k))
@@ -338,6 +351,9 @@ def poison_unused_experts(Ld, used):
     if Ld.expert_dtype == "mxfp4":
         for f in ("gate_s", "up_s", "down_s"):
             getattr(Ld, f)[poison] = 0xFF
+    elif Ld.expert_dtype == "int4g64":
+        for f in ("gate_s", "up_s", "down_s", "gate_b", "up_b", "down_b"):
+            getattr(Ld, f).view(torch.int16)[poison] = 0x7FC0   # bf16 quiet NaN scales and biases
     else:
         for f in ("gate", "up", "down"):
             getattr(Ld, f).view(torch.int16)[poison] = 0x7FC0   # bf16 quiet NaN
@@ -576,3 +592,60 @@ def test_ling_mxfp4_prefill_full_size(orc, B):
     Ld, xd = synth.device_layer(4096, 2560, 512, 8, 768, 768, "bf16", "mxfp4", "bf16", "f32", seed=3,
                                 bias="zipf")
     prefill_full_size_check(orc, B, Ld, xd, "mxfp4-prefill-4096", nrand=32, seed=1)
+
+
+# ---- group-wise affine 4-bit experts ---------------------------------------------------------
+
+@pytest.mark.parametrize("kw", [
+    dict(T=1, H=256, E=8, k=2, I=128, I_shared=64, out="f32"),
+    dict(T=4, H=512, E=32, k=4, I=192, I_shared=64, out="f32"),
+    dict(T=5, H=640, E=24, k=8, I=320, I_shared=0, out="bf16"),     # ragged rows, no shared expert
+    dict(T=16, H=2560, E=32, k=4, I=256, I_shared=64, out="f32"),   # x from global (80 KiB)
+    dict(T=2, H=4608, E=16, k=2, I=64, I_shared=64, out="f32"),     # a row longer than one slice
+])
+def test_int4_decode_small(orc, B, kw):
+    """Group-wise affine 4-bit experts on the decode path (each weight s*q + b formed in fp32)."""
+    say(f"[int4-decode] {kw}")
+    Lh, xh = synth.make_layer(**kw, act="bf16", expert="int4g64", shared="bf16", seed=12)
+    Ld, xd = synth.to_device(Lh, xh)
+    assert B.path_name(B.shape_of(Ld)) == "decode.int4g64"
+    full_check(orc, B, Lh, xh, Ld, xd, f"int4 {kw}")
+
+
+@pytest.mark.parametrize("T,out", [(1, "bf16"), (1, "f32"), (4, "bf16")])
+def test_qwen_int4_decode_full_size(orc, B, T, out):
+    """Qwen shapes (H=2048, 256 experts top-8, I=I_s=512) with the checkpoint's group-wise affine
+    4-bit experts, drawn on the device; then the unselected experts' scales and biases are
+    NaN-poisoned and the output must not change by a bit."""
+    import torch
+    say(f"[qwen-int4-decode] T={T} out={out}")
+    Ld, xd = synth.device_layer(T, 2048, 256, 8, 512, 512, "bf16", "int4g64", "bf16", out, seed=60 + T)
+    y, ids = full_check(orc, B, None, None, Ld, xd, f"qwen-int4 T={T}", copy_selected=True)
+    y0 = B.layer_forward(Ld, xd).clone()
+    poison_unused_experts(Ld, ids.ravel())
+    y1 = B.layer_forward(Ld, xd)
+    torch.cuda.synchronize()
+    assert same_bits(y0, y1)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=17, H=256, E=16, k=2, I=128, I_shared=128),
+    dict(T=64, H=512, E=32, k=4, I=192, I_shared=64, bias="zipf"),    # ragged tiles, skewed load
+    dict(T=200, H=128, E=8, k=2, I=128, I_shared=0),                  # no shared expert
+    dict(T=129, H=2048, E=64, k=8, I=512, I_shared=512, bias="zipf"),  # Qwen widths, a tile boundary
+])
+def test_int4_prefill_small(orc, B, kw):
+    """Group-wise affine 4-bit experts on the grouped-GEMM path: codes staged like MXFP4, each
+    weight rebuilt as bf16(s*q + b) between LDS and the MFMA."""
+    say(f"[int4-prefill] {kw}")
+    Lh, xh = synth.make_layer(**kw, act="bf16", expert="int4g64", shared="bf16", seed=13)
+    Ld, xd = synth.to_device(Lh, xh)
+    assert B.path_name(B.shape_of(Ld)) == "prefill.int4g64"
+    full_check(orc, B, Lh, xh, Ld, xd, f"int4-prefill {kw}")
+
+
+def test_qwen_int4_prefill_full_size(orc, B):
+    """Qwen-shaped prefill (T=4096, Zipf(1.1) expert bias) with group-wise affine 4-bit experts."""
+    say("[qwen-int4-prefill] T=4096")
+    Ld, xd = synth.device_layer(4096, 2048, 256, 8, 512, 512, "bf16", "int4g64", "bf16", "bf16", seed=4, bias="zipf")
+    prefill_full_size_check(orc, B, Ld, xd, "qwen-int4-prefill-4096", nrand=32, seed=2)
