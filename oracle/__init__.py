@@ -38,7 +38,7 @@ def build(force: bool = True) -> str:
 class _Shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "H", "E", "k", "I", "I_shared", "act_dtype", "expert_dtype",
-                 "shared_dtype")]
+                 "shared_dtype", "act_quant")]
 
 
 class _Weights(ctypes.Structure):
@@ -66,6 +66,10 @@ def lib():
         L.orc_e2m1_to_double.argtypes = [ctypes.c_uint8]
         L.orc_e8m0_to_double.restype = ctypes.c_double
         L.orc_e8m0_to_double.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_to_double.restype = ctypes.c_double
+        L.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_from_double.restype = ctypes.c_uint8
+        L.orc_e4m3_from_double.argtypes = [ctypes.c_double]
         L.orc_weight.restype = ctypes.c_double
         L.orc_weight.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
@@ -74,6 +78,8 @@ def lib():
             "orc_select": [P, ctypes.c_int, ctypes.c_int, P, P],
             "orc_set_weights": [P, ctypes.c_int, ctypes.c_int, P, P],
             "orc_plan": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P],
+            "orc_mxfp8_quantize": [P, ctypes.c_int, P, P],
+            "orc_mxfp8_dequantize": [P, P, ctypes.c_int, P],
             "orc_forward_with_routing": [P, P, P, P, P, P],
             "orc_forward": [P, P, P, P, P, P, P],
         }.items():
@@ -94,7 +100,7 @@ def _ptr(a):
 def _shape(layer) -> _Shape:
     return _Shape(layer.T, layer.H, layer.E, layer.k, layer.I, layer.I_shared,
                   _DTYPES[layer.act_dtype], _DTYPES[layer.expert_dtype],
-                  _DTYPES[layer.shared_dtype])
+                  _DTYPES[layer.shared_dtype], 1 if getattr(layer, "act_quant", "none") == "mxfp8" else 0)
 
 
 def _weights(layer) -> tuple[_Weights, list]:
@@ -123,6 +129,33 @@ def e2m1_to_double(nibble: int) -> float:
 
 def e8m0_to_double(bits: int) -> float:
     return lib().orc_e8m0_to_double(bits)
+
+
+def e4m3_to_double(bits: int) -> float:
+    return lib().orc_e4m3_to_double(bits)
+
+
+def e4m3_from_double(v: float) -> int:
+    return lib().orc_e4m3_from_double(v)
+
+
+def mxfp8_quantize(v: np.ndarray):
+    """MXFP8 (E4M3 elements, one e8m0 scale per 32): (codes uint8 [n], scales uint8 [n/32])."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    codes = np.empty(v.size, np.uint8)
+    scales = np.empty(max(v.size // 32, 1), np.uint8)
+    if lib().orc_mxfp8_quantize(_ptr(v), v.size, _ptr(codes), _ptr(scales)):
+        raise ValueError("orc_mxfp8_quantize: n must be a multiple of 32")
+    return codes, scales[: v.size // 32]
+
+
+def mxfp8_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    v = np.empty(codes.size, np.float64)
+    if lib().orc_mxfp8_dequantize(_ptr(codes), _ptr(scales), codes.size, _ptr(v)):
+        raise ValueError("orc_mxfp8_dequantize: n must be a multiple of 32")
+    return v
 
 
 def weight(base: np.ndarray, scales, dtype: str, mat, rows, cols, r, c, biases=None) -> float:

@@ -49,6 +49,76 @@ __attribute__((constructor)) static void fill_mx_tables(void) {
   for (int b = 0; b < 256; ++b) e8m0_table[b] = orc_e8m0_to_double((uint8_t)b);
 }
 
+/* OCP FP8 E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent field 0 is subnormal (mantissa * 2^-9); S.1111.111 is NaN. */
+double orc_e4m3_to_double(uint8_t bits) {
+  int sign = bits >> 7, ex = (bits >> 3) & 15, man = bits & 7;
+  double mag;
+  if (ex == 15 && man == 7) return NAN;
+  if (ex == 0)
+    mag = ldexp((double)man, -9);
+  else
+    mag = ldexp(1.0 + man / 8.0, ex - 7);
+  return sign ? -mag : mag;
+}
+
+/* Nearest E4M3 value, ties to the even mantissa, magnitudes beyond the largest
+ * finite value (448) saturating to it.  rint rounds half to even in the
+ * default rounding mode. */
+uint8_t orc_e4m3_from_double(double v) {
+  uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  double a = fabs(v);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < ldexp(1.0, -6)) /* subnormal steps of 2^-9; 8 steps is the smallest normal */
+    return sign | (uint8_t)rint(a * 512.0);
+  int e;
+  double m = frexp(a, &e); /* a = m 2^e, m in [0.5, 1): a = (1 + f) 2^(e-1) */
+  int E = e - 1;
+  double q = rint((2.0 * m - 1.0) * 8.0); /* the 3-bit mantissa, 8 = carry */
+  if (q == 8.0) {
+    q = 0.0;
+    E += 1;
+  }
+  return sign | (uint8_t)(((E + 7) << 3) | (int)q);
+}
+
+int orc_mxfp8_quantize(const double *v, int n, uint8_t *codes, uint8_t *scales) {
+  if (n % 32) return -1;
+  for (int b = 0; b < n / 32; ++b) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i)
+      if (fabs(v[32 * b + i]) > amax) amax = fabs(v[32 * b + i]);
+    int xe = -127; /* shared exponent: floor(log2 amax) - 8, in the e8m0 range */
+    if (amax > 0.0) {
+      int p;
+      frexp(amax, &p); /* amax = m 2^p, m in [0.5, 1): floor(log2 amax) = p - 1 */
+      xe = p - 1 - 8;
+      if (xe < -127) xe = -127;
+      if (xe > 127) xe = 127;
+    }
+    scales[b] = (uint8_t)(xe + 127);
+    for (int i = 0; i < 32; ++i) codes[32 * b + i] = orc_e4m3_from_double(ldexp(v[32 * b + i], -xe));
+  }
+  return 0;
+}
+
+int orc_mxfp8_dequantize(const uint8_t *codes, const uint8_t *scales, int n, double *v) {
+  if (n % 32) return -1;
+  for (int i = 0; i < n; ++i) v[i] = orc_e4m3_to_double(codes[i]) * orc_e8m0_to_double(scales[i / 32]);
+  return 0;
+}
+
+/* v[0..n) replaced by its MXFP8 quantisation, dequantised (R6c). */
+static int mxfp8_round_trip(double *v, int n) {
+  uint8_t *c = (uint8_t *)malloc((size_t)n);
+  uint8_t *s = (uint8_t *)malloc((size_t)(n / 32 + 1));
+  int rc = (c && s) ? orc_mxfp8_quantize(v, n, c, s) : -2;
+  if (rc == 0) rc = orc_mxfp8_dequantize(c, s, n, v);
+  free(c);
+  free(s);
+  return rc;
+}
+
 double orc_weight(const void *base, const void *scales, const void *biases,
                   int dtype, int64_t mat, int64_t rows, int64_t cols, int64_t r,
                   int64_t c) {
@@ -82,6 +152,7 @@ static int shape_ok(const orc_shape *s) {
     return 0;
   if (s->expert_dtype == ORC_MXFP4 && (s->H % 32 != 0 || s->I % 32 != 0)) return 0;
   if (s->expert_dtype == ORC_INT4G64 && (s->H % 64 != 0 || s->I % 64 != 0)) return 0;
+  if (s->act_quant && (s->H % 32 != 0 || s->I % 32 != 0)) return 0;
   return 1;
 }
 
@@ -183,24 +254,34 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 int orc_ffn(const double *xv, int H, int I, const void *g, const void *u,
             const void *d, const void *gs, const void *us, const void *ds,
             const void *gb, const void *ub, const void *db, int dtype,
-            int64_t mat, double *out) {
+            int64_t mat, int act_quant, double *out) {
   double *a = (double *)malloc(sizeof(double) * (size_t)I);
-  if (!a) return -2;
-  for (int i = 0; i < I; ++i) {
+  double *xq = (double *)malloc(sizeof(double) * (size_t)H);
+  if (!a || !xq) {
+    free(a);
+    free(xq);
+    return -2;
+  }
+  int rc = 0;
+  for (int h = 0; h < H; ++h) xq[h] = xv[h];
+  if (act_quant) rc = mxfp8_round_trip(xq, H); /* R6c: the gate/up input */
+  for (int i = 0; i < I && rc == 0; ++i) {
     double gi = 0.0, ui = 0.0;
     for (int h = 0; h < H; ++h) {
-      gi += orc_weight(g, gs, gb, dtype, mat, I, H, i, h) * xv[h];
-      ui += orc_weight(u, us, ub, dtype, mat, I, H, i, h) * xv[h];
+      gi += orc_weight(g, gs, gb, dtype, mat, I, H, i, h) * xq[h];
+      ui += orc_weight(u, us, ub, dtype, mat, I, H, i, h) * xq[h];
     }
     a[i] = silu(gi) * ui;
   }
-  for (int h = 0; h < H; ++h) {
+  if (rc == 0 && act_quant) rc = mxfp8_round_trip(a, I); /* R6c: the down input */
+  for (int h = 0; h < H && rc == 0; ++h) {
     double o = 0.0;
     for (int i = 0; i < I; ++i) o += orc_weight(d, ds, db, dtype, mat, H, I, h, i) * a[i];
     out[h] = o;
   }
   free(a);
-  return 0;
+  free(xq);
+  return rc;
 }
 
 int orc_forward_with_routing(const orc_shape *s, const void *x,
@@ -227,12 +308,13 @@ int orc_forward_with_routing(const orc_shape *s, const void *x,
         break;
       }
       rc = orc_ffn(xv, H, s->I, w->gate, w->up, w->down, w->gate_s, w->up_s,
-                   w->down_s, w->gate_b, w->up_b, w->down_b, s->expert_dtype, e, o);
+                   w->down_s, w->gate_b, w->up_b, w->down_b, s->expert_dtype, e,
+                   s->act_quant, o);
       for (int h = 0; h < H; ++h) yt[h] += cw[(int64_t)t * s->k + j] * o[h];
     }
     if (rc == 0 && s->I_shared > 0) {
       rc = orc_ffn(xv, H, s->I_shared, w->sh_gate, w->sh_up, w->sh_down, NULL,
-                   NULL, NULL, NULL, NULL, NULL, s->shared_dtype, 0, o);
+                   NULL, NULL, NULL, NULL, NULL, s->shared_dtype, 0, 0, o);
       for (int h = 0; h < H; ++h) yt[h] += o[h];
     }
   }

@@ -51,6 +51,17 @@
  *     elements of a row along the reduction index; the weight is s*q + b,
  *     taken exactly (the page's kernel rounds it to bfloat16 before its
  *     multiply; that rounding belongs to the kernel, not to the weight).
+ *  R6c W4A8 numerics ("Three ways to boost mixture-of-experts inference on
+ *     NVIDIA DGX Spark", section "Why decoding was slow in the first place":
+ *     the baseline serves MXFP4 expert weights with 8-bit activations): with
+ *     act_quant = 1 the input of each routed expert's two GEMMs (x before
+ *     gate/up, a before down) is replaced by its MXFP8 quantisation (OCP MX
+ *     v1.0): per 32 consecutive elements along the reduction index a shared
+ *     scale X = 2^(floor(log2(amax)) - 8) (8 = the largest exponent of an E4M3
+ *     element; clamped to the e8m0 range 2^-127 .. 2^127, a block of zeros
+ *     takes 2^-127) and elements P = E4M3(v / X), rounded to nearest even and
+ *     saturated to +-448 (OCP FP8 E4M3: bias 7, no infinities, S.1111.111 is
+ *     NaN).  The router and the shared expert are not quantised.
  *  R7 routing plan: per-expert counts, exclusive offsets, and slots
  *     (slot = t*k + j) ordered by expert by a stable counting sort.
  *
@@ -75,6 +86,7 @@ typedef struct {
   int32_t act_dtype;    /* ORC_F32 | ORC_BF16 */
   int32_t expert_dtype; /* ORC_F32 | ORC_BF16 | ORC_MXFP4 | ORC_INT4G64 */
   int32_t shared_dtype; /* ORC_F32 | ORC_BF16 */
+  int32_t act_quant;    /* 0: none; 1: MXFP8 inputs of the routed experts' GEMMs (R6c) */
 } orc_shape;
 
 typedef struct {
@@ -92,6 +104,13 @@ typedef struct {
 double orc_bf16_to_double(uint16_t bits);
 double orc_e2m1_to_double(uint8_t nibble);   /* low 4 bits used */
 double orc_e8m0_to_double(uint8_t bits);     /* 2^(bits-127); NaN for 0xFF */
+double orc_e4m3_to_double(uint8_t bits);     /* OCP FP8 E4M3; NaN for S.1111.111 */
+uint8_t orc_e4m3_from_double(double v);      /* round to nearest even, saturating */
+
+/* R6c: MXFP8 quantisation of n (a multiple of 32) values: codes[n] E4M3,
+ * scales[n/32] e8m0.  And its inverse. */
+int orc_mxfp8_quantize(const double *v, int n, uint8_t *codes, uint8_t *scales);
+int orc_mxfp8_dequantize(const uint8_t *codes, const uint8_t *scales, int n, double *v);
 
 /* Element (row r, column c) of matrix `mat` of a stacked [n_mat][rows][cols]
  * weight array in the given encoding (cols is the reduction dimension). */
@@ -121,7 +140,7 @@ int orc_plan(const int32_t *ids, int T, int k, int E, int32_t *counts,
 int orc_ffn(const double *xv, int H, int I, const void *g, const void *u,
             const void *d, const void *gs, const void *us, const void *ds,
             const void *gb, const void *ub, const void *db, int dtype,
-            int64_t mat, double *out);
+            int64_t mat, int act_quant, double *out);
 
 /* R4 + R5 with the routing given: y[T][H] (double). */
 int orc_forward_with_routing(const orc_shape *s, const void *x,

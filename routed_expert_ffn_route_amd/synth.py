@@ -74,6 +74,7 @@ class Layer:
     gate_b: object = None       # INT4 only: bf16 biases [E][I][H/64]
     up_b: object = None
     down_b: object = None       # [E][H][I/64]
+    act_quant: str = "none"     # "mxfp8": the routed experts' GEMM inputs quantised to MXFP8 (W4A8)
 
     def with_T(self, T: int) -> "Layer":
         return dataclasses.replace(self, T=T)

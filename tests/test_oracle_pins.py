@@ -462,3 +462,84 @@ def test_hand_worked_example(orc):
     assert ids.tolist() == [[0, 1]] and lg.tolist() == [[2.0, 1.0, 0.0]]
     assert np.allclose(w[0], [w0, w1], rtol=1e-15)
     assert np.allclose(y[0], want, rtol=1e-14)
+
+
+# --- MXFP8 activations (W4A8) -----------------------------------------------------------------
+
+def test_e4m3_decode_matches_torch_float8(orc):
+    """All 256 E4M3 codes against torch's float8_e4m3fn (an independent library decoder)."""
+    import torch
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for c in range(256):
+        assert _same(orc.e4m3_to_double(c), float(ref[c])), hex(c)
+    assert orc.e4m3_to_double(0x7E) == 448.0 and orc.e4m3_to_double(0x08) == 2.0 ** -6
+    assert orc.e4m3_to_double(0x01) == 2.0 ** -9 and math.isnan(orc.e4m3_to_double(0xFF))
+
+
+def test_e4m3_rounding_matches_torch_and_saturates(orc):
+    """In range, the encoder rounds like torch's float -> float8_e4m3fn cast (nearest, ties to
+    even), exact midpoints and subnormals included; beyond 448 it saturates (the cast would give
+    NaN there)."""
+    import torch
+    rng = np.random.default_rng(21)
+    grid = torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    mids = (grid[1:] + grid[:-1]) / 2                       # every tie between neighbours
+    vals = np.concatenate([rng.uniform(-440, 440, 4000), rng.uniform(-2 ** -6, 2 ** -6, 2000),
+                           mids, -mids, grid, [0.0, -0.0, 447.9, 448.0]])
+    want = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for v, w in zip(vals, want):
+        assert orc.e4m3_from_double(float(v)) == int(w), v
+    for v in (448.0001, 463.9, 464.0, 500.0, 1e30):
+        assert orc.e4m3_from_double(v) == 0x7E and orc.e4m3_from_double(-v) == 0xFE
+
+
+def test_mxfp8_scale_rule_and_round_trip(orc):
+    """The shared scale is 2^(floor(log2 amax) - 8): a block whose amax is 2^k gets e8m0 byte
+    127 + k - 8 and its amax element becomes 256 (code 0x78); a block with amax in [1.75, 2) 2^k
+    saturates its largest element to 448; a zero block gets byte 0 and zero codes; values on the
+    grid (E4M3 codes times a power of two, the largest with exponent 8) round-trip exactly."""
+    rng = np.random.default_rng(22)
+    for k in (-20, -3, 0, 5, 30):
+        v = rng.uniform(-1, 1, 32) * 2.0 ** k * 0.9
+        v[7] = 2.0 ** k
+        c, s = orc.mxfp8_quantize(v)
+        assert s[0] == 127 + k - 8 and c[7] == 0x78
+        v[7] = -1.9 * 2.0 ** k
+        c, s = orc.mxfp8_quantize(v)
+        assert s[0] == 127 + k - 8 and c[7] == 0xFE
+    c, s = orc.mxfp8_quantize(np.zeros(64))
+    assert np.all(s == 0) and np.all(c == 0)
+    for trial in range(50):
+        e = int(rng.integers(-30, 30))
+        codes = rng.integers(0, 0x7F, 32).astype(np.uint8) | rng.choice([0, 0x80], 32).astype(np.uint8)
+        codes[int(rng.integers(32))] = 0x78 + int(rng.integers(0, 7))   # largest element: exponent field 15 (2^8)
+        v = np.array([orc.e4m3_to_double(int(b)) for b in codes]) * 2.0 ** e
+        c, s = orc.mxfp8_quantize(v)
+        back = orc.mxfp8_dequantize(c, s)
+        assert s[0] == 127 + e and np.array_equal(back, v)
+
+
+def test_w4a8_dense_expert_quantises_both_gemm_inputs(orc):
+    """E = 1, k = 1, a shared expert: with MXFP8 activations the routed expert computes
+    Wd Q(silu(Wg Q(x)) * (Wu Q(x))), Q the quantise-dequantise round trip (pinned above), with
+    the MXFP4 weights decoded by the spec table; the shared expert is left unquantised.  Checked
+    against numpy matmuls."""
+    import dataclasses
+    L, x = synth.make_layer(2, 128, 1, 1, 64, 32, "bf16", "mxfp4", "bf16", "f32", seed=23)
+    Lq = dataclasses.replace(L, act_quant="mxfp8")
+    y, ids, w, _ = orc.forward(Lq, x)
+    xs = _np_w(x, "bf16")
+    Wg, Wu, Wd = _np_mx(L.gate, L.gate_s)[0], _np_mx(L.up, L.up_s)[0], _np_mx(L.down, L.down_s)[0]
+    Sg, Su, Sd = _np_w(L.sh_gate, "bf16"), _np_w(L.sh_up, "bf16"), _np_w(L.sh_down, "bf16")
+
+    def q(v):
+        return orc.mxfp8_dequantize(*orc.mxfp8_quantize(v))
+    for t in range(2):
+        xq = q(xs[t])
+        g, u = Wg @ xq, Wu @ xq
+        a = q(g * scipy.special.expit(g) * u)
+        want = Wd @ a + _np_ffn(xs[t], Sg, Su, Sd)
+        assert np.allclose(y[t], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    y_plain = orc.forward(L, x)[0]
+    rel = np.linalg.norm(y - y_plain) / np.linalg.norm(y_plain)
+    assert 1e-3 < rel < 1e-1, rel    # the quantisation is there, and of the expected size
