@@ -20,6 +20,7 @@ table the rocprofv3 summaries under profiles/ are computed from as well.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import statistics
@@ -133,6 +134,8 @@ def main():
         Ld, xd = synth.device_layer(T, spec["H"], spec["E"], spec["k"], spec["I"], spec["I_shared"],
                                     spec["act"], spec["expert"], spec["shared"], spec["out"], seed=li,
                                     bias=spec["bias"], d=spec["d"])
+        if spec.get("act_quant"):
+            Ld = dataclasses.replace(Ld, act_quant=spec["act_quant"])
         layers.append((Ld, xd, B.weights_of(Ld)))
     torch.cuda.synchronize()
     shape = B.shape_of(layers[0][0])
@@ -248,7 +251,7 @@ def main():
         if wk["bound"] == "hbm":
             amount, ach, peak, unit = wk["bytes"], wk["bytes"] / dom_s / 1e9, W.HBM_PEAK_GBS, "GB/s"
         else:
-            amount, ach, peak, unit = wk["flops"], wk["flops"] / dom_s / 1e12, W.BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
+            amount, ach, peak, unit = wk["flops"], wk["flops"] / dom_s / 1e12, wk["peak_tflops"], "TFLOP/s"
         prof = profile_record(dom, args.workload, T)
         roof = {"bound": wk["bound"], "achieved": round(ach, 1), "peak": peak, "unit": unit,
                 "frac": round(ach / peak, 4), "traffic": prof["traffic_bytes"] if prof else None,

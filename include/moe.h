@@ -93,7 +93,21 @@ typedef struct {
   int32_t expert_dtype; /* gate/up/down: MOE_F32 | MOE_BF16 | MOE_MXFP4 | MOE_INT4G64 */
   int32_t shared_dtype; /* shared expert: MOE_F32 | MOE_BF16                   */
   int32_t out_dtype;    /* y:          MOE_F32 | MOE_BF16                      */
+  int32_t act_quant;    /* MOE_QNONE, or MOE_QMXFP8: W4A8 numerics             */
 } moe_shape_t;
+
+/* act_quant.  MOE_QMXFP8 ("Three ways to boost mixture-of-experts inference
+ * on NVIDIA DGX Spark", section "Why decoding was slow in the first place":
+ * MXFP4 expert weights with 8-bit activations): the input of each routed
+ * expert's two GEMMs -- x before gate/up, the SwiGLU activations before down --
+ * is quantised to MXFP8 (OCP MX v1.0: per 32 consecutive elements along the
+ * reduction index an e8m0 scale 2^(floor(log2 amax) - 8), clamped to the e8m0
+ * range, and E4M3 elements rounded to nearest even, saturated at +-448), and
+ * both GEMMs run on gfx950's block-scaled fp8 x fp4 matrix cores.  The router
+ * and the shared expert stay unquantised.  Needs MXFP4 experts, bf16
+ * activations and T > 16 (the grouped-GEMM path); else MOE_EUNSUPPORTED. */
+#define MOE_QNONE 0
+#define MOE_QMXFP8 1
 
 typedef struct {
   const float *router_w;     /* [E][H], required                               */

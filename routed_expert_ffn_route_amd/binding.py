@@ -20,7 +20,7 @@ EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_static
 class Shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "H", "E", "k", "I", "I_shared", "act_dtype", "expert_dtype", "shared_dtype",
-                 "out_dtype")]
+                 "out_dtype", "act_quant")]
 
 
 class Weights(ctypes.Structure):
@@ -96,7 +96,7 @@ def _ptr(t):
 def shape_of(layer) -> Shape:
     return Shape(layer.T, layer.H, layer.E, layer.k, layer.I, layer.I_shared,
                  DTYPES[layer.act_dtype], DTYPES[layer.expert_dtype], DTYPES[layer.shared_dtype],
-                 DTYPES[layer.out_dtype])
+                 DTYPES[layer.out_dtype], 1 if getattr(layer, "act_quant", "none") == "mxfp8" else 0)
 
 
 def weights_of(layer) -> Weights:

@@ -37,6 +37,8 @@ int check_shape(const moe_shape_t* s) {
   if (!f32 && !b16) return MOE_EUNSUPPORTED;
   if (s->expert_dtype == MOE_INT4G64 && (s->H % 64 || s->I % 64)) return MOE_EUNSUPPORTED;
   if (s->out_dtype != MOE_F32 && s->out_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (s->act_quant != MOE_QNONE && s->act_quant != MOE_QMXFP8) return MOE_EUNSUPPORTED;
+  if (s->act_quant == MOE_QMXFP8 && (s->expert_dtype != MOE_MXFP4 || s->T <= kDecodeMaxT)) return MOE_EUNSUPPORTED;
   if (s->T > kDecodeMaxT) {  // prefill path
     if (s->act_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
     // MXFP4 / INT4G64 experts: the scale (and bias) rows of a weight tile are staged in LDS
@@ -72,7 +74,8 @@ Layout layout(const moe_shape_t* s) {
   } else {
     L.pf = off;
     off += up(prefill_ws_bytes(s->T, s->H, s->E, s->k, s->I, s->I_shared,
-                               s->expert_dtype == MOE_MXFP4 || s->expert_dtype == MOE_INT4G64));
+                               s->expert_dtype == MOE_MXFP4 || s->expert_dtype == MOE_INT4G64,
+                               s->act_quant == MOE_QMXFP8));
   }
   L.total = off;
   return L;
@@ -91,6 +94,7 @@ Args make_args(const moe_shape_t* s, const void* x, const moe_weights_t* w, void
   A.wdt = s->expert_dtype;
   A.sdt = s->shared_dtype;
   A.odt = s->out_dtype;
+  A.aq = s->act_quant;
   A.x = x;
   A.rw = w->router_w;
   A.rbias = w->router_bias;
@@ -290,7 +294,7 @@ const char* moe_path_name(const moe_shape_t* shape) {
   switch (shape->expert_dtype) {
     case MOE_F32: return dec ? "decode.f32" : "prefill.f32";
     case MOE_BF16: return dec ? "decode.bf16" : "prefill.bf16";
-    case MOE_MXFP4: return dec ? "decode.mxfp4" : "prefill.mxfp4";
+    case MOE_MXFP4: return dec ? "decode.mxfp4" : shape->act_quant == MOE_QMXFP8 ? "prefill.mxfp4.w4a8" : "prefill.mxfp4";
     case MOE_INT4G64: return dec ? "decode.int4g64" : "prefill.int4g64";
   }
   return "invalid";

@@ -17,6 +17,7 @@ constexpr int kDecodeMaxT = 16;     // T at or below this takes the decode (GEMV
 struct Args {
   int T, H, E, k, I, Is;
   int act, wdt, sdt, odt;             // moe_dtype_t of x, experts, shared, y
+  int aq;                             // act_quant: MOE_QNONE | MOE_QMXFP8
   const void* x;
   const float* rw;
   const float* rbias;

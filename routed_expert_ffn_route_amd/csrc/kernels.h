@@ -53,7 +53,7 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook);
 
 // Workspace bytes needed by the prefill path's sections; precise: MXFP4 or INT4G64 experts
 // (activations as bf16 hi + lo parts, fp32 slot rows).
-size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is, bool precise);
+size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is, bool precise, bool w4a8);
 int prefill_tiles_cap(int T, int E, int k);
 constexpr int kPfTileRows = 128;  // rows per grouped-GEMM tile (the block map's unit)
 

@@ -53,7 +53,11 @@ int pf_router_splits(int T, int H, int E) {
   return std::max(1, std::min(want, most));
 }
 
-size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is, bool precise) {
+// W4A8: row strides of the MXFP8 scale arrays (one byte per 32 elements, padded to 16 bytes
+// so that a row's scales stage into LDS with 16-byte loads)
+inline int mx8_scale_ld(int K) { return (K / 32 + 15) / 16 * 16; }
+
+size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is, bool precise, bool w4a8) {
   const size_t S = (size_t)T * k, R = S + T;
   const size_t Imax = I > Is ? I : Is;
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
@@ -63,7 +67,9 @@ size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is, bool precise)
          up(sizeof(int) * 4 * (size_t)prefill_tiles_cap(T, E, k)) + up(256) + np * up(2 * R * Imax) +
          up(2 * np * R * (size_t)H) + up(2 * 3 * (size_t)E * H) +
          (ks > 1 ? up(sizeof(float) * (size_t)ks * T * E) : 0) +
-         up(sizeof(int) * (size_t)permute_blocks(T, k) * E);
+         up(sizeof(int) * (size_t)permute_blocks(T, k) * E) +
+         (w4a8 ? up((size_t)T * H) + up((size_t)T * mx8_scale_ld(H)) + up(R * Imax) + up(R * mx8_scale_ld((int)Imax))
+               : 0);
 }
 
 // Upper bound of sum over the E+1 groups of ceil(rows / kPfBM).
@@ -87,6 +93,12 @@ struct PfLayout {
   float* rpart;      // [ks][T][E] partial router logits (K split ks > 1 ways), else null
   int ks;
   int* bcnt;         // [permute_blocks][E] per-block expert counts of the permutation
+  // W4A8 (MXFP8 activations): x and the routed activations as E4M3 codes + e8m0 scales
+  uint8_t* xq;       // [T][H]
+  uint8_t* xs;       // [T][xs_ld]
+  uint8_t* aq;       // [S+T][Imax] grouped order (routed rows)
+  uint8_t* as;       // [S+T][as_ld]
+  int xs_ld, as_ld;
 };
 
 PfLayout pf_layout(const Args& A) {
@@ -122,6 +134,19 @@ PfLayout pf_layout(const Args& A) {
   L.rpart = L.ks > 1 ? (float*)b : nullptr;
   if (L.ks > 1) b += up(sizeof(float) * (size_t)L.ks * A.T * A.E);
   L.bcnt = (int*)b;
+  b += up(sizeof(int) * (size_t)permute_blocks(A.T, A.k) * A.E);
+  L.xs_ld = mx8_scale_ld(A.H);
+  L.as_ld = mx8_scale_ld((int)Imax);
+  L.xq = L.xs = L.aq = L.as = nullptr;
+  if (A.aq == MOE_QMXFP8) {
+    L.xq = b;
+    b += up((size_t)A.T * A.H);
+    L.xs = b;
+    b += up((size_t)A.T * L.xs_ld);
+    L.aq = b;
+    b += up(R * Imax);
+    L.as = b;
+  }
   return L;
 }
 
@@ -604,6 +629,275 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// W4A8: MXFP8 activations against MXFP4 weights on gfx950's block-scaled matrix cores
+// ("Three ways to boost mixture-of-experts inference on NVIDIA DGX Spark", section "Why
+// decoding was slow in the first place": MXFP4 expert weights with 8-bit activations).  MXFP8
+// per OCP MX v1.0: per 32 elements a scale 2^(floor(log2 amax) - 8) (8: the largest exponent of
+// an E4M3 value), clamped to the e8m0 range, and E4M3 elements rounded to nearest even,
+// saturated at +-448 (the input is clamped first; the hardware conversion then rounds to
+// nearest even).
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ int mx8_exp(float amax) {
+  if (!(amax > 0.f)) return -127;  // a block of zeros
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 9;  // frexp: amax = m 2^p, m in [0.5, 1)
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+__device__ __forceinline__ float mx8_clamp(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
+// four values (already divided by the block scale) -> four E4M3 codes, first in the low byte
+__device__ __forceinline__ uint32_t mx8_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(mx8_clamp(a), mx8_clamp(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(mx8_clamp(c), mx8_clamp(d), w, true);
+}
+
+// x [T][H] bf16 -> E4M3 codes xq [T][H] and e8m0 scales xs [T][xs_ld]; one 32-element block per
+// thread.
+__global__ __launch_bounds__(256) void pf_quant_x(Args A, PfLayout L) {
+  const int nb = A.H / 32;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)A.T * nb) return;
+  const int t = (int)(i / nb), blk = (int)(i % nb);
+  const uint4* src = (const uint4*)((const uint16_t*)A.x + (size_t)t * A.H + (size_t)blk * 32);
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 u = src[q];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * q + 2 * j] = bf16lo(w[j]);
+      v[8 * q + 2 * j + 1] = bf16hi(w[j]);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  const int xe = mx8_exp(amax);
+  uint32_t c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    c[j] = mx8_pack4(ldexpf(v[4 * j], -xe), ldexpf(v[4 * j + 1], -xe), ldexpf(v[4 * j + 2], -xe),
+                     ldexpf(v[4 * j + 3], -xe));
+  uint4* dst = (uint4*)(L.xq + (size_t)t * A.H + (size_t)blk * 32);
+  dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+  dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+  L.xs[(size_t)t * L.xs_ld + blk] = (uint8_t)(xe + 127);
+}
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// The grouped GEMM for W4A8, routed tiles only: 128 x 256 block tiles as pf_gemm, K-steps of 64
+// (one v_mfma_scale_f32_32x32x64_f8f6f4 per 32 x 32 tile), a three-deep LDS ring filled by
+// buffer loads to LDS: A = 128 rows x 64 E4M3 codes (the row XOR swizzle of pf_gemm, 64-byte
+// rows), B = 256 rows x 64 e2m1 codes (32 bytes).  The e8m0 scales of the tile's A rows and of
+// each wave's 64 B rows are staged once per tile.  Operand layout of the instruction: A lane
+// (row, h) holds K [16h, 16h + 16) and [32 + 16h, 32 + 16h + 16), B lane (column, h) holds K
+// [32h, 32h + 32), and lane (row or column, h) supplies the scale of the 32-block h.
+// MODE 0 gate/up: A = the tile's token rows of xq, epilogue SwiGLU -> MXFP8 activations (aq, as).
+// MODE 1 down: A = the tile's rows of aq; epilogue: fp32 rows weighted by the routing weight.
+template <int MODE, int NS>
+__global__ __launch_bounds__(2 * kPfBM, 2) void pf_gemm_w4a8(Args A, PfLayout L, int nb_per_tile, int nblocks,
+                                                               int /*part: the routed tiles only*/) {
+  constexpr int BM = kPfBM;
+  constexpr int kUA = BM * 64 / 16;        // 16-byte units of A per stage (128 rows x 64 bytes)
+  constexpr int kUB = kPfBN * 32 / 16;     // of B (256 rows x 32 bytes)
+  constexpr int kStage = kUA + kUB;
+  extern __shared__ __attribute__((aligned(16))) uint4 smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
+  const int shtiles = A.Is > 0 ? (A.T + BM - 1) / BM : 0;
+  const int ntl = *L.ntiles - shtiles;  // the routed groups' tiles come first in the map
+  const int nreal = min(nblocks, ntl * nb_per_tile);
+  if ((int)blockIdx.x >= nreal) return;
+  const int b = xcd_swizzle(blockIdx.x, nreal);
+  const int ti = b / nb_per_tile, nb = b - ti * nb_per_tile;
+  const int4 tl = ((const int4*)L.tiles)[ti];  // {group, first row, rows, 0}
+  const int g = tl.x, pos0 = tl.y, nrows = tl.z;
+  const int K = MODE == 0 ? A.H : A.I, N = MODE == 0 ? A.I : A.H;
+  const int n0 = MODE == 0 ? nb * (kPfBN / 2) : nb * kPfBN;
+  if (n0 >= N) return;
+  const int S = A.T * A.k;
+  const size_t Imax = A.I > A.Is ? A.I : A.Is;
+  const int ald = MODE == 0 ? L.xs_ld : L.as_ld;  // A scale bytes per row (padded)
+
+  // ---- A: per lane two 16-byte units per step (rows r = p / 4, chunk (p % 4) ^ swizzle)
+  i32x4_t ra, ras;
+  uint32_t ao[2];
+  if constexpr (MODE == 0) {
+    ra = buf_rsrc(L.xq, (size_t)A.T * A.H);
+    ras = buf_rsrc(L.xs, (size_t)A.T * L.xs_ld);
+  } else {
+    ra = buf_rsrc(L.aq + (size_t)pos0 * Imax, (size_t)nrows * Imax);
+    ras = buf_rsrc(L.as + (size_t)pos0 * L.as_ld, (size_t)nrows * L.as_ld);
+  }
+  auto a_row = [&](int r) -> int {  // the A row of tile row r in its array (-1: past the tile)
+    if (r >= nrows) return -1;
+    if constexpr (MODE == 0) {
+      const int slot = L.rows[pos0 + r];
+      return slot / A.k;  // routed tiles only: slot < S
+    }
+    return r;
+  };
+  const uint32_t a_ld = MODE == 0 ? (uint32_t)A.H : (uint32_t)Imax;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = (wave * 2 + j) * 64 + lane, r = p >> 2, c = (p & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
+    const int ar = a_row(r);
+    ao[j] = ar < 0 ? kOOB : (uint32_t)ar * a_ld + c * 16u;
+  }
+  // ---- B: per lane two 16-byte units per step (row p / 2, half p % 2)
+  i32x4_t rb[2];
+  uint32_t bo[2];
+  i32x4_t rs;
+  uint32_t so = 0;  // the wave's first B scale row's offset (uniform)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = (wave * 2 + j) * 64 + lane, r = p >> 1, c = p & 1;
+    uint32_t rowb = kOOB;
+    if constexpr (MODE == 0) {
+      const int half = r >> 7, jj = r & 127;
+      const bool up = jj >> 6;  // uniform per instruction
+      const int col = n0 + half * 64 + (jj & 63);
+      rb[j] = buf_rsrc((const uint8_t*)(up ? A.up : A.gate) + (size_t)g * A.I * (A.H / 2), (size_t)N * (A.H / 2));
+      if (col < N) rowb = (uint32_t)col * (A.H / 2);
+    } else {
+      const int hh = n0 + r;
+      rb[j] = buf_rsrc((const uint8_t*)A.down + (size_t)g * A.H * (A.I / 2), (size_t)A.H * (K / 2));
+      if (hh < A.H) rowb = (uint32_t)hh * (K / 2);
+    }
+    bo[j] = rowb == kOOB ? kOOB : rowb + c * 16u;
+  }
+  const int sb = K / 32, sbi = (64 * sb + 1023) / 1024, wstr = sbi * 1024;  // B scale bytes per row / per wave
+  if constexpr (MODE == 0) {
+    const bool up = wave & 1;  // wave w stages B rows 64 w ... : half w / 2, gate (w even) or up
+    rs = buf_rsrc((const uint8_t*)(up ? A.us : A.gs) + (size_t)g * A.I * (A.H / 32), (size_t)N * (A.H / 32));
+    so = (uint32_t)(n0 + (wave >> 1) * 64) * (A.H / 32);
+  } else {
+    rs = buf_rsrc((const uint8_t*)A.ds + (size_t)g * A.H * (A.I / 32), (size_t)A.H * (K / 32));
+    so = (uint32_t)(n0 + wave * 64) * (K / 32);
+  }
+  uint8_t* s_bs = (uint8_t*)(smem + NS * kStage);      // [4 waves][wstr]
+  uint8_t* s_as = s_bs + 4 * wstr;                     // [BM rows][ald]
+  const int nk = K / 64;
+  auto issue = [&](int st, uint4* stage) {
+    const uint32_t ks = (uint32_t)(st < nk ? st : nk - 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(ra, ao[j] + ks * 64u, lds_addr(stage + (wave * 2 + j) * 64));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(rb[j], bo[j] + ks * 32u, lds_addr(stage + kUA + (wave * 2 + j) * 64));
+  };
+  // scales first (the first stage's wait covers them): the wave's 64 B rows, then the tile's A rows
+  for (int i = 0; i < sbi; ++i)
+    dma16(rs, so + (uint32_t)(i * 64 + lane) * 16u, lds_addr((uint4*)(s_bs + (size_t)wave * wstr) + i * 64));
+  {
+    const int upr = ald / 16, nu = BM * upr;  // 16-byte units per A scale row / per tile
+    for (int u0 = wave * 64; u0 < nu; u0 += 4 * 64) {  // uniform trip count per wave
+      const int u = u0 + lane, r = u / upr, cu = u - r * upr;
+      const int ar = u < nu ? a_row(r) : -1;
+      const uint32_t off = ar < 0 ? kOOB : (uint32_t)ar * (uint32_t)ald + cu * 16u;
+      dma16(ras, off, lds_addr((uint4*)s_as + u0));
+    }
+  }
+  __shared__ int s_slot[BM];
+  __shared__ float s_wt[BM];
+  if constexpr (MODE == 1) {
+    if (tid < nrows) {
+      const int slot = L.rows[pos0 + tid];
+      s_slot[tid] = slot;
+      s_wt[tid] = A.cw[slot];
+    }
+  }
+  const int mlive = min(2, max(0, (nrows - wm * 64 + 31) / 32));
+  f32x16_t acc[2][4] = {};
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) issue(i, smem + i * kStage);
+  for (int s = 0; s < nk; ++s) {
+    wait_vm<4 * (NS - 2)>();  // this wave's loads of step s (and the scales) have landed
+    __syncthreads();
+    issue(s + NS - 1, smem + ((s + NS - 1) % NS) * kStage);
+    const uint4* st = smem + (s % NS) * kStage;
+    i32x8_t af[2];
+    int sa[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int row = wm * 64 + m * 32 + (lane & 31);
+      const uint4 u0 = st[swz_unit(row, h)], u1 = st[swz_unit(row, 2 + h)];
+      af[m] = i32x8_t{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+      sa[m] = s_as[row * ald + 2 * s + h];
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int br = wn * 128 + n * 32 + (lane & 31);
+      const uint4 u = st[kUA + br * 2 + h];
+      const i32x8_t bf = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+      const int sbv = s_bs[(br >> 6) * wstr + (br & 63) * sb + 2 * s + h];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (m >= mlive) break;  // uniform
+        acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[m], bf, acc[m][n], 0, 4, 0, sa[m], 0, sbv);
+      }
+    }
+  }
+  wait_vm<0>();
+
+  // ---- epilogue; C row = wm * 64 + m * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4, column lane % 32
+  if constexpr (MODE == 0) {
+    // SwiGLU, then MXFP8 per 32 activation columns of a row: the 32 lanes of a half-wave hold one
+    // such block, so its amax is a reduction over them; codes go through LDS for 16-byte stores
+    constexpr int LDB = kPfBN / 2 + 16;  // bytes per LDS row
+    uint8_t* ct = (uint8_t*)smem;
+    __syncthreads();  // every wave is done with the ring
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+          const float v = silu_fast(acc[m][pr][r]) * acc[m][2 + pr][r];
+          float am = fabsf(v);
+          am = fmaxf(am, dpp_f<kDppXor1>(am));
+          am = fmaxf(am, dpp_f<kDppXor2>(am));
+          am = fmaxf(am, dpp_f<kDppHalfMirror>(am));
+          am = fmaxf(am, dpp_f<kDppMirror>(am));
+          am = fmaxf(am, __shfl_xor(am, 16, 64));
+          const int xe = mx8_exp(am);
+          const int code = __builtin_amdgcn_cvt_pk_fp8_f32(mx8_clamp(ldexpf(v, -xe)), 0.f, 0, false) & 0xFF;
+          const int colb = wn * 64 + pr * 32;  // the block's first column in the tile
+          ct[row * LDB + colb + (lane & 31)] = (uint8_t)code;
+          if ((lane & 31) == 0 && row < nrows && n0 + colb < N)
+            L.as[(size_t)(pos0 + row) * L.as_ld + (n0 + colb) / 32] = (uint8_t)(xe + 127);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int UPR = (kPfBN / 2) / 16;  // 16-byte units per tile row
+    for (int u = tid; u < nrows * UPR; u += 2 * BM) {
+      const int rr = u / UPR, cu = u - rr * UPR, col = n0 + cu * 16;
+      if (col >= N) continue;
+      *(uint4*)&L.aq[(size_t)(pos0 + rr) * Imax + col] = *(const uint4*)&ct[rr * LDB + cu * 16];
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+        if (row >= nrows) continue;
+        const float wt = s_wt[row];
+        float* orow = L.outf + (size_t)s_slot[row] * A.H;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int col = n0 + wn * 128 + n * 32 + (lane & 31);
+          if (col < N) orow[col] = wt * acc[m][n][r];
+        }
+      }
+    }
+  }
+  (void)S;
+}
+
 __global__ __launch_bounds__(256) void pf_select(Args A, const float* rpart, int ks) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -716,7 +1010,18 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   if (rc) return rc;
   const int cap = prefill_tiles_cap(A.T, A.E, A.k);
   const int Imax = A.I > A.Is ? A.I : A.Is;
-  const bool f4 = A.wdt == MOE_MXFP4, i4 = A.wdt == MOE_INT4G64;
+  const bool f4 = A.wdt == MOE_MXFP4, i4 = A.wdt == MOE_INT4G64, w4a8 = A.aq == MOE_QMXFP8;
+  // W4A8 LDS: the ring, the four waves' B scale blocks, the tile's A scale rows
+  auto w4a8_lds = [&](int K) {
+    const size_t ring = (size_t)kPfNS * (kPfBM * 64 + kPfBN * 32);
+    return ring + (size_t)4 * ((64 * (K / 32) + 1023) / 1024) * 1024 + (size_t)kPfBM * mx8_scale_ld(K);
+  };
+  if (w4a8) {  // x -> MXFP8 for the routed gate/up GEMM
+    void* aq[] = {&A, &L};
+    if (launch(hook, "pf_quant_x", (const void*)pf_quant_x, dim3((unsigned)(((size_t)A.T * (A.H / 32) + 255) / 256)),
+               dim3(256), aq, 0, st) != hipSuccess)
+      return MOE_EHIP;
+  }
   // MXFP4 experts: the routed groups' tiles run the MXFP4 kernel, the shared expert's tiles the
   // bf16 kernel, both in the precise variant (activation hi + lo parts, fp32 slot rows).
   // INT4G64 experts: the routed tiles run the int4 kernel (weights rebuilt in bf16 on the way
@@ -731,7 +1036,12 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   const int shtiles = A.Is > 0 ? (A.T + kPfBM - 1) / kPfBM : 0;
   {
     const int nbt = (Imax + kPfBN / 2 - 1) / (kPfBN / 2);
-    if (i4) {
+    if (w4a8) {
+      rc = run("pf_gateup", (const void*)pf_gemm_w4a8<0, kPfNS>, cap * nbt, nbt, 1, w4a8_lds(A.H));
+      if (!rc && shtiles)
+        rc = run("pf_gateup_shared", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, true>, shtiles * nbt, nbt, 2,
+                 pf_lds<0, kPfNS, MOE_BF16, true>(A.H));
+    } else if (i4) {
       rc = run("pf_gateup", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_INT4G64, true>, cap * nbt, nbt, 1,
                pf_lds<0, kPfNS, MOE_INT4G64, true>(A.H));
       if (!rc && shtiles)
@@ -750,7 +1060,12 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   }
   {
     const int nbt = (A.H + kPfBN - 1) / kPfBN;
-    if (i4) {
+    if (w4a8) {
+      rc = run("pf_down", (const void*)pf_gemm_w4a8<1, kPfNS>, cap * nbt, nbt, 1, w4a8_lds(A.I));
+      if (!rc && shtiles)
+        rc = run("pf_down_shared", (const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, true>, shtiles * nbt, nbt, 2,
+                 pf_lds<1, kPfNSG, MOE_BF16, true>(A.Is));
+    } else if (i4) {
       rc = run("pf_down", (const void*)pf_gemm<1, kPfBM, kPfNS, MOE_INT4G64, true>, cap * nbt, nbt, 1,
                pf_lds<1, kPfNS, MOE_INT4G64, true>(A.I));
       if (!rc && shtiles)

@@ -32,13 +32,15 @@ KERNEL_SOURCES = {
     "pf_": ["csrc/prefill.hip", "csrc/route.hip", "csrc/select.h", "csrc/common.h", "csrc/kernels.h"],
 }
 # bench label -> regular expression over the demangled kernel name rocprofv3 reports
-# (pf_gemm<MODE, BM, NS, weight dtype, precise>; dtype 1 = bf16, 2 = MXFP4)
+# (pf_gemm<MODE, BM, NS, weight dtype, precise>; dtype 1 = bf16, 2 = MXFP4, 3 = int4; pf_gemm_w4a8<MODE, NS>)
 KERNEL_SYMBOLS = {
     "dec_router": r"dec_router<", "dec_select": r"dec_select<", "dec_gateup": r"dec_gateup<",
     "dec_down": r"dec_down<",
     "pf_router_split": r"pf_split_router\(", "pf_router": r"pf_gemm<2, ",
-    "pf_gateup": r"pf_gemm<0, \d+, \d+, (1, false|2, true)>", "pf_gateup_shared": r"pf_gemm<0, \d+, \d+, 1, true>",
-    "pf_down": r"pf_gemm<1, \d+, \d+, (1, false|2, true)>", "pf_down_shared": r"pf_gemm<1, \d+, \d+, 1, true>",
+    "pf_gateup": r"pf_gemm<0, \d+, \d+, (1, false|2, true|3, true)>|pf_gemm_w4a8<0,",
+    "pf_gateup_shared": r"pf_gemm<0, \d+, \d+, 1, true>",
+    "pf_down": r"pf_gemm<1, \d+, \d+, (1, false|2, true|3, true)>|pf_gemm_w4a8<1,",
+    "pf_down_shared": r"pf_gemm<1, \d+, \d+, 1, true>", "pf_quant_x": r"pf_quant_x\(",
     "pf_select": r"pf_select\(", "pf_combine": r"pf_combine\(",
 }
 
@@ -101,7 +103,7 @@ def main():
         "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
         "source_hash": source_hash(a.kernel),
     }
-    peak = 8000.0 if wk["bound"] == "hbm" else 2500.0
+    peak = 8000.0 if wk["bound"] == "hbm" else wk.get("peak_tflops", 2500.0)
     frac = (out["gbs_algorithmic"] if wk["bound"] == "hbm" else out["tflops"]) / peak
     out["frac"] = round(frac, 4)
     cmds = open(a.commands).read().strip()
@@ -115,7 +117,7 @@ def main():
     if wk["bound"] == "hbm":
         print(f"* achieved: {alg_b / avg_ns:.1f} GB/s on algorithmic bytes = {frac:.3f} of 8000 GB/s")
     else:
-        print(f"* achieved: {alg_f / avg_ns / 1e3:.1f} TFLOP/s = {frac:.3f} of 2500 TFLOP/s bf16")
+        print(f"* achieved: {alg_f / avg_ns / 1e3:.1f} TFLOP/s = {frac:.3f} of {peak:g} TFLOP/s")
     print(f"* FETCH_SIZE per dispatch: {fetch_kib:.1f} KiB (median of {len(kf)}); "
           f"WRITE_SIZE: {write_kib:.1f} KiB (median of {len(kw)})")
     print(f"* copy calibration: a {a.copy_bytes} B device copy reads {statistics.median(cf):.1f} KiB "

@@ -14,6 +14,7 @@ from __future__ import annotations
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
+FP8_MFMA_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 matrix cores (the W4A8 GEMMs' fp8 x fp4 rate)
 
 
 def workload_spec(name, T_override=None, d=32):
@@ -41,6 +42,9 @@ def workload_spec(name, T_override=None, d=32):
     if name == "qwen_int4_prefill":
         return dict(T=T_override or 4096, H=2048, E=256, k=8, I=512, I_shared=512, act="bf16", expert="int4g64",
                     shared="bf16", out="bf16", bias="zipf", d=None, layers=8)
+    if name == "ling_w4a8_prefill":   # Ling MXFP4 experts with MXFP8 activations
+        return dict(T=T_override or 4096, H=2560, E=512, k=8, I=768, I_shared=768, act="bf16", expert="mxfp4",
+                    shared="bf16", out="f32", bias="zipf", d=None, layers=8, act_quant="mxfp8")
     if name == "tiny":
         return dict(T=T_override or 4, H=256, E=16, k=2, I=128, I_shared=128, act="f32", expert="f32",
                     shared="f32", out="f32", bias=None, d=None, layers=1)
@@ -109,4 +113,14 @@ def kernel_work(spec, distinct):
         "pf_down_shared": ("mfma", sh_dn + T * (Is * ab + H * rb), 2.0 * T * Is * H),
         "pf_combine": ("hbm", (S + T) * H * rb + T * H * ys, 0.0),
     }
-    return {n: {"bound": b, "bytes": int(by), "flops": float(f)} for n, (b, by, f) in w.items()}
+    if spec.get("act_quant") == "mxfp8":   # W4A8: 1-byte activations + a scale byte per 32
+        xq = T * H + T * H // 32
+        w["pf_quant_x"] = ("hbm", T * H * 2 + xq, 0.0)
+        w["pf_gateup"] = ("mfma", distinct * gu + xq + S * I + S * I // 32, 4.0 * S * I * H)
+        w["pf_down"] = ("mfma", distinct * dn + S * I + S * I // 32 + S * H * rb, 2.0 * S * I * H)
+    out = {n: {"bound": b, "bytes": int(by), "flops": float(f)} for n, (b, by, f) in w.items()}
+    for n, v in out.items():   # the matrix-core peak each GEMM is measured against
+        if v["bound"] == "mfma":
+            v["peak_tflops"] = (FP8_MFMA_PEAK_TFLOPS if spec.get("act_quant") == "mxfp8" and n in ("pf_gateup", "pf_down")
+                                else BF16_MFMA_PEAK_TFLOPS)
+    return out

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def _shape(**kw):
     base = dict(T=1, H=2048, E=256, k=8, I=512, I_shared=512, act_dtype=1, expert_dtype=1,
-                shared_dtype=1, out_dtype=1)
+                shared_dtype=1, out_dtype=1, act_quant=0)
     base.update(kw)
     return B.Shape(*[base[n] for n, _ in B.Shape._fields_])
 
@@ -68,6 +68,9 @@ def test_strerror_covers_codes(lib):
     # group-wise affine 4-bit: groups of 64 along H and I
     (dict(expert_dtype=3, H=2048 + 32), B.MOE_EUNSUPPORTED), (dict(expert_dtype=3, I=512 + 32), B.MOE_EUNSUPPORTED),
     (dict(expert_dtype=3, act_dtype=0, shared_dtype=0), B.MOE_EUNSUPPORTED),
+    # W4A8: MXFP4 experts on the grouped-GEMM path only
+    (dict(T=64, act_quant=1), B.MOE_EUNSUPPORTED), (dict(T=4, expert_dtype=2, act_quant=1), B.MOE_EUNSUPPORTED),
+    (dict(T=64, expert_dtype=3, act_quant=1), B.MOE_EUNSUPPORTED), (dict(T=64, expert_dtype=2, act_quant=2), B.MOE_EUNSUPPORTED),
 ])
 def test_shape_validation(lib, kw, code):
     rc, _ = _ws(_shape(**kw))
@@ -82,6 +85,7 @@ def test_workspace_sizes_and_paths(lib):
                      (dict(T=4096, H=2560, E=512, I=768, I_shared=768, expert_dtype=2, out_dtype=0),
                       "prefill.mxfp4"), (dict(T=64, expert_dtype=2, H=8192), "prefill.mxfp4"),
                      (dict(expert_dtype=3), "decode.int4g64"), (dict(T=4096, expert_dtype=3), "prefill.int4g64"),
+                     (dict(T=4096, expert_dtype=2, out_dtype=0, act_quant=1), "prefill.mxfp4.w4a8"),
                      (dict(T=4, H=256, E=16, k=2, I=128, I_shared=128, act_dtype=0, expert_dtype=0,
                            shared_dtype=0, out_dtype=0), "decode.f32")]:
         s = _shape(**kw)

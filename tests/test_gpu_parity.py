@@ -20,6 +20,10 @@ Bars (floating point compared with the oracle's double-precision result):
     each weight in bf16 before its multiply, as the page's kernel does, one more rounding of up to
     2^-9 in each of the two GEMMs than a bf16 layer has (expected relative L2 about 3e-3; the
     largest of 8M elements near 6 standard deviations of that, about 1.8e-2);
+  * W4A8 (MXFP8 activations for the routed experts' GEMMs, MXFP4 weights): relative L2 <= 1e-3
+    against the oracle that quantises the same activations (both sides round each E4M3 code to
+    nearest even from nearly equal values, and the fp8 x fp4 products are exact; the differences
+    are fp32 accumulation and a rare code that a near-tie rounds the other way);
   * all-fp32 layer: relative L2 <= 1e-5 (fp32 accumulation over <= 2^12 terms stays
     near 1e-6).
 """
@@ -75,7 +79,9 @@ def check_out(L, y, ref, tag):
     max_rel, l2 = errs(y, ref)
     say(f"[{tag}] max_rel={max_rel:.3e} rel_l2={l2:.3e}")
     assert np.all(np.isfinite(y)), tag
-    if L.expert_dtype == "mxfp4":
+    if getattr(L, "act_quant", "none") == "mxfp8":
+        assert l2 <= 1e-3, tag
+    elif L.expert_dtype == "mxfp4":
         assert L.out_dtype == "f32", "the MXFP4 bar is stated on an fp32 output"
         assert l2 <= 1e-3, tag
     elif L.expert_dtype == "int4g64" and L.T <= 16 and L.out_dtype == "f32":
@@ -649,3 +655,33 @@ def test_qwen_int4_prefill_full_size(orc, B):
     say("[qwen-int4-prefill] T=4096")
     Ld, xd = synth.device_layer(4096, 2048, 256, 8, 512, 512, "bf16", "int4g64", "bf16", "bf16", seed=4, bias="zipf")
     prefill_full_size_check(orc, B, Ld, xd, "qwen-int4-prefill-4096", nrand=32, seed=2)
+
+
+# ---- W4A8: MXFP8 activations on the block-scaled fp8 x fp4 matrix cores ------------------------
+
+@pytest.mark.parametrize("kw", [
+    dict(T=17, H=256, E=16, k=2, I=128, I_shared=128),
+    dict(T=64, H=512, E=32, k=4, I=192, I_shared=64, bias="zipf"),    # ragged tiles, skewed load
+    dict(T=200, H=128, E=8, k=2, I=128, I_shared=0),                  # no shared expert
+    dict(T=160, H=1024, E=4, k=2, I=512, I_shared=512, bias="zipf"),  # hot experts span 2 tiles
+    dict(T=20, H=2560, E=16, k=4, I=768, I_shared=768),               # Ling widths
+])
+def test_w4a8_prefill_small(orc, B, kw):
+    """MXFP4 experts with MXFP8 activations (x and the SwiGLU activations quantised per 32) against
+    the quantising oracle; the error against the unquantised layer is printed for scale."""
+    say(f"[w4a8-prefill] {kw}")
+    Lh, xh = synth.make_layer(**kw, act="bf16", expert="mxfp4", shared="bf16", out="f32", seed=14)
+    Lh = dataclasses.replace(Lh, act_quant="mxfp8")
+    Ld, xd = synth.to_device(Lh, xh)
+    assert B.path_name(B.shape_of(Ld)) == "prefill.mxfp4.w4a8"
+    y, ids = full_check(orc, B, Lh, xh, Ld, xd, f"w4a8 {kw}")
+    plain = orc.forward(dataclasses.replace(Lh, act_quant="none"), xh)[0]
+    say(f"  vs the unquantised layer: rel_l2={np.linalg.norm(y - plain) / np.linalg.norm(plain):.3e}")
+
+
+def test_ling_w4a8_prefill_full_size(orc, B):
+    """Ling-shaped MXFP4 prefill with MXFP8 activations (T=4096, 512 experts top-8, Zipf load)."""
+    say("[ling-w4a8-prefill] T=4096")
+    Ld, xd = synth.device_layer(4096, 2560, 512, 8, 768, 768, "bf16", "mxfp4", "bf16", "f32", seed=5, bias="zipf")
+    Ld = dataclasses.replace(Ld, act_quant="mxfp8")
+    prefill_full_size_check(orc, B, Ld, xd, "w4a8-prefill-4096", nrand=16, seed=3)
