@@ -102,9 +102,11 @@ template <> struct GUC<MOE_MXFP4, MOE_BF16> {
     deq4(w.w, d.v + 12);
     return d;
   }
+  // CS: bytes from one 32-element chunk of x to the next (64, or 80 in the padded LDS layout)
+  template <int CS = 64>
   static __device__ __forceinline__ void dot(const D& g, const D& u, const uint8_t* xrow, int c,
                                              float sg, float su, float& ag, float& au) {
-    const uint8_t* xp = xrow + (size_t)c * 64;
+    const uint8_t* xp = xrow + (size_t)c * CS;
     float a = 0.f, b = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -148,9 +150,10 @@ template <> struct GUC<MOE_INT4G64, MOE_BF16> {
     return d;
   }
   // sg, su: the scales (0 for a masked chunk); cg, cu: b - 128 s
+  template <int CS = 64>
   static __device__ __forceinline__ void dot(const D& g, const D& u, const uint8_t* xrow, int c, float sg,
                                              float cg, float su, float cu, float& ag, float& au) {
-    const uint8_t* xp = xrow + (size_t)c * 64;
+    const uint8_t* xp = xrow + (size_t)c * CS;
     float a = 0.f, b = 0.f, x = 0.f;
     constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
 #pragma unroll
@@ -199,14 +202,19 @@ __device__ __forceinline__ void x_rows_load(uint4 (&xr)[kXB], int base, int n, i
     }
   }
 }
+// XP (x of 4-bit experts): every 64-byte chunk (32 bf16) is followed by 16 bytes of padding in
+// LDS, so that the G lanes of a group, which read chunks c, c + 1, ..., start 20 banks apart
+// instead of 16 (64-byte strides put every fourth lane on the same banks).
+template <bool XP>
 __device__ __forceinline__ void x_rows_store(const uint4 (&xr)[kXB], int base, int n, int rw,
                                              unsigned mask, uint4* xs) {
+  const int rwl = XP ? rw / 4 * 5 : rw;
 #pragma unroll
   for (int j = 0; j < kXB; ++j) {
     const int i = base + j * (int)blockDim.x;
     if (i < n) {
-      const int q = i / rw, t = nth_token(mask, q);
-      xs[t * rw + (i - q * rw)] = xr[j];
+      const int q = i / rw, t = nth_token(mask, q), u = i - q * rw;
+      xs[t * rwl + (XP ? (u >> 2) * 5 + (u & 3) : u)] = xr[j];
     }
   }
 }
@@ -225,6 +233,7 @@ __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* u
                                            size_t xstride, unsigned mask, const int* slots,
                                            float* out, int out_ld, int row, int gl, bool valid) {
   typedef GUC<WT, XT> C;
+  constexpr bool XP = XL && (WT == MOE_MXFP4 || WT == MOE_INT4G64);  // padded x rows in LDS
   float ag[TM], au[TM];
 #pragma unroll
   for (int t = 0; t < TM; ++t) ag[t] = au[t] = 0.f;
@@ -258,15 +267,16 @@ __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* u
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (XL) {
       if (c0 == 0) {  // the rows of the tokens in `mask` only
-        x_rows_store(xr, threadIdx.x, xn, rw, mask, xs);
+        x_rows_store<XP>(xr, threadIdx.x, xn, rw, mask, xs);
         for (int base = threadIdx.x + kXB * blockDim.x; base < xn; base += kXB * blockDim.x) {
           x_rows_load(xr, base, xn, rw, mask, xg, xstride);
-          x_rows_store(xr, base, xn, rw, mask, xs);
+          x_rows_store<XP>(xr, base, xn, rw, mask, xs);
         }
         __syncthreads();
       }
     }
     const uint8_t* xb = XL ? (const uint8_t*)xs : xg;
+    const size_t xrs = XP ? (size_t)(rw / 4 * 5) * 16 : xstride;  // bytes per x row where it is read
 #pragma unroll
     for (int m = 0; m < NCH; ++m) {
       const typename C::D dg = C::deq(wg[m]), du = C::deq(wu[m]);
@@ -287,9 +297,11 @@ __device__ __forceinline__ void gateup_row(const uint8_t* grow, const uint8_t* u
       for (int t = 0; t < TM; ++t) {
         if (!((mask >> t) & 1u)) continue;  // uniform
         if constexpr (WT == MOE_INT4G64)
-          C::dot(dg, du, xb + (size_t)t * xstride, cc[m], sg, cg, su, cu, ag[t], au[t]);
+          C::template dot<XP ? 80 : 64>(dg, du, xb + (size_t)t * xrs, cc[m], sg, cg, su, cu, ag[t], au[t]);
+        else if constexpr (WT == MOE_MXFP4)
+          C::template dot<XP ? 80 : 64>(dg, du, xb + (size_t)t * xrs, cc[m], sg, su, ag[t], au[t]);
         else
-          C::dot(dg, du, xb + (size_t)t * xstride, cc[m], sg, su, ag[t], au[t]);
+          C::dot(dg, du, xb + (size_t)t * xrs, cc[m], sg, su, ag[t], au[t]);
       }
     }
   }
@@ -363,8 +375,10 @@ template <> struct DN<MOE_MXFP4> {
     acc = dword_dot(w.z, x[4], x[5], acc);
     return dword_dot(w.w, x[6], x[7], acc);
   }
+  // CS: floats from one chunk's activations to the next (32, or 36 in the padded LDS layout)
+  template <int CS = 32>
   static __device__ __forceinline__ float dot(W w, const float* a, int c) {
-    const float* p = a + (size_t)c * 32;
+    const float* p = a + (size_t)c * CS;
     float acc = dword_dot(w.x, ldf4(p), ldf4(p + 4), 0.f);
     acc = dword_dot(w.y, ldf4(p + 8), ldf4(p + 12), acc);
     acc = dword_dot(w.z, ldf4(p + 16), ldf4(p + 20), acc);
@@ -391,8 +405,9 @@ template <> struct DN<MOE_INT4G64> {
     }
     return acc;
   }
+  template <int CS = 32>
   static __device__ __forceinline__ float dot_affine(W w, const float* a, int c, float s, float b) {
-    const float* p = a + (size_t)c * 32;
+    const float* p = a + (size_t)c * CS;
     float acc = dword_dot(w.x, ldf4(p), ldf4(p + 4), s, b, 0.f);
     acc = dword_dot(w.y, ldf4(p + 8), ldf4(p + 12), s, b, acc);
     acc = dword_dot(w.z, ldf4(p + 16), ldf4(p + 20), s, b, acc);
@@ -744,6 +759,11 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
   float* s_ash = s_f + ash_off;
 
   const int nch = A.I / DN<WT>::EPC;
+  // 4-bit experts with activations in LDS: 4 floats of padding after every 32-float chunk, so
+  // that the G lanes of a group (chunks c, c + 1, ...) start 36 banks apart rather than 32
+  constexpr bool AP = ALDS && DN<WT>::EPC == 32;
+  constexpr int kCS = AP ? 36 : DN<WT>::EPC;  // floats per chunk where the routed rows are read
+  const int ldr = ALDS ? nch * kCS : A.I;     // floats per routed activation row there
   const int nsl = (nch + G * NCH - 1) / (G * NCH);
   const int nchs = A.Is / DN<SWT>::EPC;
   const int nsls = (nchs + G * NCH - 1) / (G * NCH);
@@ -841,7 +861,7 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
     }
     const unsigned mask = sh ? all_t : s_m[u];
     const float* ab = sh ? asbase : abase;
-    const int ld = sh ? A.Is : A.I;
+    const int ld = sh ? A.Is : ldr;
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       if (!((mask >> t) & 1u)) continue;  // uniform
@@ -855,7 +875,9 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
           d = DN<WT>::dot(bf.w[m], arow, cc[m]);
         else if constexpr (WT == MOE_INT4G64)
           d = sh ? DN<SWT>::dot(bf.w[m], arow, cc[m])
-                 : DN<WT>::dot_affine(bf.w[m], arow, cc[m], bf16lo(bf.sb[m]), bf16hi(bf.sb[m]));
+                 : DN<WT>::template dot_affine<kCS>(bf.w[m], arow, cc[m], bf16lo(bf.sb[m]), bf16hi(bf.sb[m]));
+        else if constexpr (WT == MOE_MXFP4)
+          d = sh ? DN<SWT>::dot(bf.w[m], arow, cc[m]) : DN<WT>::template dot<kCS>(bf.w[m], arow, cc[m]);
         else
           d = sh ? DN<SWT>::dot(bf.w[m], arow, cc[m]) : DN<WT>::dot(bf.w[m], arow, cc[m]);
         part = fmaf(sc[m], d, part);
@@ -908,8 +930,15 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
     }
   }
   for (int i = tid; i < nrgb_max * NW * TM * RB; i += bd) s_part[i] = 0.f;
-  // staging unit i: routed activations [S][I] for i < n4, then the shared ones [T][I_s]
-  auto stage_dst = [&](int i) { return i < n4 ? (float4*)s_act + i : (float4*)s_ash + (i - n4); };
+  // staging unit i: routed activations [S][I] for i < n4 (AP: into the padded rows), then the
+  // shared ones [T][I_s]
+  const int q4 = A.I / 4;  // float4 units per routed row
+  auto stage_dst = [&](int i) {
+    if (i >= n4) return (float4*)s_ash + (i - n4);
+    if constexpr (!AP) return (float4*)s_act + i;
+    const int r = i / q4, q = i - r * q4;
+    return (float4*)(s_act + (size_t)r * ldr + (q >> 3) * kCS) + (q & 7);
+  };
 #pragma unroll
   for (int j = 0; j < kStg; ++j) {
     const int i = tid + j * bd;
@@ -1071,6 +1100,9 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   const size_t xbytes = (size_t)A.T * A.H * (XT == MOE_F32 ? 4 : 2);
   static_assert((size_t)MOE_MAX_H * 4 <= (size_t)kMaxLdsX, "a single token's x fits in LDS");
   const bool xl = TM == 1 || xbytes <= kMaxLdsX;
+  // 4-bit experts read x from padded LDS rows (16 bytes after every 64)
+  constexpr bool w4 = WT == MOE_MXFP4 || WT == MOE_INT4G64;
+  const size_t xbytes_gu = w4 ? xbytes / 4 * 5 : xbytes;
   // shared expert gate/up: one row per wave, in the selection kernel (T > 1) or beside the
   // routed rows of the gate/up kernel (T = 1)
   const int sh_waves = TM == 1 ? kWaves : TM;
@@ -1097,7 +1129,7 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   else
     f2 = xl ? gateup_fn<XT, WT, SWT, TM, GUL, true, false>(g2) : gateup_fn<XT, WT, SWT, TM, GUL, false, false>(g2);
   void* args2[] = {&A, &tiles, &sh_blocks};
-  err = launch(hook, "dec_gateup", f2, dim3(sh_blocks + D * tiles), dim3(kThreads), args2, xl ? xbytes : 0, st);
+  err = launch(hook, "dec_gateup", f2, dim3(sh_blocks + D * tiles), dim3(kThreads), args2, xl ? xbytes_gu : 0, st);
   if (err != hipSuccess) return MOE_EHIP;
 
   // down: at most one block per CU, each over an even share of the row groups
@@ -1109,7 +1141,9 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   constexpr int nw = 16;
   const size_t plan_w = 2 * (size_t)D + 2 * (size_t)D * A.T;
   int act_off = (int)((plan_w + (size_t)nrgb * nw * TM * rb3 + 3) / 4 * 4);
-  int ash_off = (int)(act_off + ((size_t)S * A.I + 3) / 4 * 4);
+  // routed activations in LDS; 4-bit experts pad each 32-float chunk to 36 floats
+  const size_t act_floats = w4 ? (size_t)S * (A.I / 32) * 36 : (size_t)S * A.I;
+  int ash_off = (int)(act_off + (act_floats + 3) / 4 * 4);
   const size_t lds_act = (size_t)ash_off * 4 + (size_t)A.T * A.Is * 4;
   const bool alds = lds_act <= (size_t)dv.max_lds;
   const size_t lds3 = alds ? lds_act : (size_t)act_off * 4;

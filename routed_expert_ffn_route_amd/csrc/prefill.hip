@@ -28,6 +28,7 @@
 // a three-deep LDS ring that the buffer unit fills directly (loads to LDS, no register
 // staging), rows XOR-swizzled so that MFMA fragment reads are free of bank conflicts.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -463,20 +464,30 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
   // rows of this wave that hold data (uniform): skip MFMA tiles wholly past the tile end
   const int mlive = min(2, max(0, (nrows - wm * 64 + 31) / 32));
   f32x16_t acc[2][4] = {};
-  auto step = [&](int s) {
+  // One K-step: wait for its stage, refill the ring, then the fragment reads of the step (both
+  // 16-deep halves, or one half at a time with a two-stage ring) before their MFMAs, so that
+  // the reads' latency overlaps the first MFMAs.  ML = the wave's live 32-row groups, a constant inside the loop (the loop is
+  // instantiated per value), so nothing branches between the MFMAs.
+  auto step = [&](auto ml_c, int s) {
+    constexpr int ML = decltype(ml_c)::value;
     wait_vm<(kNA + kNB) * (NS - 2)>();  // this wave's loads of step s have landed (later ones in flight)
     __syncthreads();          // ... and every other wave's; all are done with step s - 1's stage
     issue(s + NS - 1, smem + ((s + NS - 1) % NS) * kStage);
+    if constexpr (ML == 0) return;
     const uint4* st = smem + (s % NS) * kStage;
+    // two-stage rings run three blocks per CU: one half's fragments at a time
+    constexpr int KB = NS >= 3 ? 2 : 1;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int kb = 0; kb < 2; kb += KB) {
+    bf16x8_t af[2][2], afl[2][2], bfr[2][4];
+#pragma unroll
+    for (int ks = kb; ks < kb + KB; ++ks) {
       const int c = ks * 2 + (lane >> 5);
-      bf16x8_t af[2], afl[2], bfr[4];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        af[m] = __builtin_bit_cast(bf16x8_t, st[swz_unit(wm * 64 + m * 32 + (lane & 31), c)]);
+      for (int m = 0; m < ML; ++m) {
+        af[ks][m] = __builtin_bit_cast(bf16x8_t, st[swz_unit(wm * 64 + m * 32 + (lane & 31), c)]);
         if constexpr (C::AHL)
-          afl[m] = __builtin_bit_cast(bf16x8_t, st[C::kUnitsA + swz_unit(wm * 64 + m * 32 + (lane & 31), c)]);
+          afl[ks][m] = __builtin_bit_cast(bf16x8_t, st[C::kUnitsA + swz_unit(wm * 64 + m * 32 + (lane & 31), c)]);
       }
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
@@ -494,7 +505,7 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
             const f2 w2 = {fmaf(gs, (float)((ev >> (8 * p)) & 0xFFu), gb), fmaf(gs, (float)((od >> (8 * p)) & 0xFFu), gb)};
             v[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, b2));
           }
-          bfr[n] = __builtin_bit_cast(bf16x8_t, make_uint4(v[0], v[1], v[2], v[3]));
+          bfr[ks][n] = __builtin_bit_cast(bf16x8_t, make_uint4(v[0], v[1], v[2], v[3]));
         } else if constexpr (F4) {  // 8 codes of this lane's K range, scaled while unpacked to bf16
           const uint32_t q = ((const uint32_t*)(st + kStageA + br))[c];
           const float sc = e8m0_to_f32(s_sc[(br >> 6) * wtot + (br & 63) * sb + s0 + s]);
@@ -503,25 +514,37 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
           v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1));
           v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 2));
           v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 3));
-          bfr[n] = __builtin_bit_cast(bf16x8_t, make_uint4(v[0], v[1], v[2], v[3]));
+          bfr[ks][n] = __builtin_bit_cast(bf16x8_t, make_uint4(v[0], v[1], v[2], v[3]));
         } else {
-          bfr[n] = __builtin_bit_cast(bf16x8_t, st[kStageA + swz_unit(br, c)]);
+          bfr[ks][n] = __builtin_bit_cast(bf16x8_t, st[kStageA + swz_unit(br, c)]);
         }
       }
+    }
+    // every read of the batch is issued before its first MFMA (two-stage rings: left to the
+    // scheduler, which keeps the registers within three blocks per CU)
+    if constexpr (NS >= 3) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (m >= mlive) break;  // uniform
+    for (int ks = kb; ks < kb + KB; ++ks)
+#pragma unroll
+      for (int m = 0; m < ML; ++m)
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-          acc[m][n] = mfma32(af[m], bfr[n], acc[m][n]);
-          if constexpr (C::AHL) acc[m][n] = mfma32(afl[m], bfr[n], acc[m][n]);
+          acc[m][n] = mfma32(af[ks][m], bfr[ks][n], acc[m][n]);
+          if constexpr (C::AHL) acc[m][n] = mfma32(afl[ks][m], bfr[ks][n], acc[m][n]);
         }
-      }
     }
   };
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) issue(i, smem + i * kStage);
-  for (int s = 0; s < nk; ++s) step(s);
+  typedef std::integral_constant<int, 0> ML0;
+  typedef std::integral_constant<int, 1> ML1;
+  typedef std::integral_constant<int, 2> ML2;
+  if (mlive == 2)  // uniform
+    for (int s = 0; s < nk; ++s) step(ML2{}, s);
+  else if (mlive == 1)
+    for (int s = 0; s < nk; ++s) step(ML1{}, s);
+  else
+    for (int s = 0; s < nk; ++s) step(ML0{}, s);
   wait_vm<0>();  // no load may still write this block's LDS after it retires
 
   // ---- epilogue; C row = wm * 64 + m * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4
