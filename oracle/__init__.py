@@ -21,6 +21,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# MOE_ORACLE_LIB: load another build of oracle.c instead (the sanitizer test's ASan/UBSan build)
+_LOAD = os.environ.get("MOE_ORACLE_LIB") or _LIB
 
 F32, BF16, MXFP4, INT4G64 = 0, 1, 2, 3
 _DTYPES = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "int4g64": INT4G64}
@@ -33,6 +35,27 @@ def build(force: bool = True) -> str:
                "-fPIC", "-shared", "-Wall", "-Wextra", "-o", _LIB, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
     return _LIB
+
+
+CLANG = "/opt/rocm/llvm/bin/clang"
+
+
+def build_sanitized(outdir: str) -> str:
+    """Compile oracle.c with clang under AddressSanitizer + UndefinedBehaviorSanitizer (any
+    report aborts) into outdir/liboracle_san.so; loading it needs the clang ASan runtime
+    preloaded (asan_runtime())."""
+    os.makedirs(outdir, exist_ok=True)
+    out = os.path.join(outdir, "liboracle_san.so")
+    cmd = [CLANG, "-std=c99", "-O1", "-g", "-fno-omit-frame-pointer", "-ffp-contract=off",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-shared-libsan",
+           "-fPIC", "-shared", "-o", out, _SRC, "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out
+
+
+def asan_runtime() -> str:
+    return subprocess.run([CLANG, "-print-file-name=libclang_rt.asan-x86_64.so"], check=True,
+                          capture_output=True, text=True).stdout.strip()
 
 
 class _Shape(ctypes.Structure):
@@ -56,9 +79,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if _LOAD == _LIB and not os.path.exists(_LIB):
             build(force=True)
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(_LOAD)
         P = ctypes.c_void_p
         L.orc_bf16_to_double.restype = ctypes.c_double
         L.orc_bf16_to_double.argtypes = [ctypes.c_uint16]

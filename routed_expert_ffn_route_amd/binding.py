@@ -8,7 +8,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe.so")
+# MOE_LIB: load another build of the library (the sanitizer test's host-instrumented build)
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 STATIC_SCRATCH_BYTES = 32 << 20   # MOE_STATIC_SCRATCH_BYTES

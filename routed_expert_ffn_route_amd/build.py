@@ -54,5 +54,28 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizer build (ASan + UBSan) of the C-ABI unit for the CPU tests: api.hip is
+# recompiled with the host pass instrumented (the device code is unchanged) and linked with the
+# other objects of the last build().  Loading it needs the clang ASan runtime preloaded.
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized(outdir: str) -> str:
+    objs = [os.path.join(OBJ, u[1]) for u in SOURCES if u[0] != "api.hip"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"run build() first: {missing[0]} is missing")
+    os.makedirs(outdir, exist_ok=True)
+    api = os.path.join(outdir, "api_san.o")
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g"]
+    subprocess.run([HIPCC, *flags, *SAN_HOST, "-c", os.path.join(CSRC, "api.hip"), "-o", api],
+                   check=True, capture_output=True)
+    lib = os.path.join(outdir, "libmoe_san.so")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *SAN_HOST, "-Xarch_host", "-shared-libsan",
+                    "-o", lib, api, *objs], check=True, capture_output=True)
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
