@@ -1032,19 +1032,21 @@ int pick_gn(const GN (&list)[N], int nchunks, bool first_fit = false) {
 // Down config: among entries leaving at most a quarter of their chunk slots idle, the one
 // whose busiest block has the fewest rounds of work items over its 16 waves (a wave keeps
 // two items in flight, so rounds, not rows, set the latency chain), counting D distinct
-// experts' and the shared expert's items; ties go to more chunks per lane (more bytes in
-// flight), then list order.  Else the fewest idle slots.
+// experts' and the shared expert's items; ties go to fewer idle chunk slots (idle lanes
+// still execute the dot products, which bound the 4-bit kernels), then to more chunks per
+// lane (more bytes in flight), then list order.  Else the fewest idle slots.
 int pick_down(int nch, int nchs, int H, int D, int ncu) {
-  int best = -1, score = 1 << 30, bnch = 0;
+  int best = -1, score = 1 << 30, bidle = 0, bnch = 0;
   for (int i = 0; i < kNDN; ++i) {
     const int cap = kDN[i].G * kDN[i].NCH;
     if (cap < nch || 4 * (cap - nch) > cap) continue;
     const int rb = kWave / kDN[i].G, nrg = (H + rb - 1) / rb, nrgb = (nrg + ncu - 1) / ncu;
     const int items = nrgb * (((nch + cap - 1) / cap) * D + (nchs + cap - 1) / cap);
-    const int sc = (items + 15) / 16;
-    if (sc < score || (sc == score && kDN[i].NCH > bnch)) {
+    const int sc = (items + 15) / 16, idle = cap - nch;
+    if (best < 0 || sc < score || (sc == score && (idle < bidle || (idle == bidle && kDN[i].NCH > bnch)))) {
       best = i;
       score = sc;
+      bidle = idle;
       bnch = kDN[i].NCH;
     }
   }
