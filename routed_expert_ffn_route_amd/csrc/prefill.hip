@@ -835,15 +835,19 @@ __global__ __launch_bounds__(2 * kPfBM, 2) void pf_gemm_w4a8(Args A, PfLayout L,
   f32x16_t acc[2][4] = {};
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) issue(i, smem + i * kStage);
-  for (int s = 0; s < nk; ++s) {
+  // one K-step: ML = the wave's live 32-row groups, a constant inside the loop (instantiated per
+  // value); every operand read of the step is issued before its first MFMA
+  auto step = [&](auto ml_c, int s) {
+    constexpr int ML = decltype(ml_c)::value;
     wait_vm<4 * (NS - 2)>();  // this wave's loads of step s (and the scales) have landed
     __syncthreads();
     issue(s + NS - 1, smem + ((s + NS - 1) % NS) * kStage);
+    if constexpr (ML == 0) return;
     const uint4* st = smem + (s % NS) * kStage;
-    i32x8_t af[2];
-    int sa[2];
+    i32x8_t af[2], bfr[4];
+    int sa[2], sbv[4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < ML; ++m) {
       const int row = wm * 64 + m * 32 + (lane & 31);
       const uint4 u0 = st[swz_unit(row, h)], u1 = st[swz_unit(row, 2 + h)];
       af[m] = i32x8_t{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
@@ -853,15 +857,25 @@ __global__ __launch_bounds__(2 * kPfBM, 2) void pf_gemm_w4a8(Args A, PfLayout L,
     for (int n = 0; n < 4; ++n) {
       const int br = wn * 128 + n * 32 + (lane & 31);
       const uint4 u = st[kUA + br * 2 + h];
-      const i32x8_t bf = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-      const int sbv = s_bs[(br >> 6) * wstr + (br & 63) * sb + 2 * s + h];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (m >= mlive) break;  // uniform
-        acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[m], bf, acc[m][n], 0, 4, 0, sa[m], 0, sbv);
-      }
+      bfr[n] = i32x8_t{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+      sbv[n] = s_bs[(br >> 6) * wstr + (br & 63) * sb + 2 * s + h];
     }
-  }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int m = 0; m < ML; ++m)
+        acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[m], bfr[n], acc[m][n], 0, 4, 0, sa[m], 0, sbv[n]);
+  };
+  typedef std::integral_constant<int, 0> ML0;
+  typedef std::integral_constant<int, 1> ML1;
+  typedef std::integral_constant<int, 2> ML2;
+  if (mlive == 2)  // uniform
+    for (int s = 0; s < nk; ++s) step(ML2{}, s);
+  else if (mlive == 1)
+    for (int s = 0; s < nk; ++s) step(ML1{}, s);
+  else
+    for (int s = 0; s < nk; ++s) step(ML0{}, s);
   wait_vm<0>();
 
   // ---- epilogue; C row = wm * 64 + m * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4, column lane % 32
