@@ -282,9 +282,10 @@ struct PfCfg {
   static constexpr size_t ring_bytes = (size_t)NS * kStage * 16;
 };
 
+// The body of one GEMM block; bid: the block's index among the launch's blocks of this kind.
 template <int MODE, int BM, int NS, int WT, bool P>
-__global__ __launch_bounds__(2 * BM, BM == 128 ? (NS == 2 ? 3 : 2) : 1)
-void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
+__device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, int nb_per_tile, int nblocks,
+                                             int part, int bid) {
   typedef PfCfg<MODE, BM, NS, WT, P> C;
   constexpr bool F4 = C::F4, I4 = C::I4;
   constexpr int kStageA = C::kStageA, kStage = C::kStage, kNA = C::kNA, kNB = C::kNB;
@@ -300,8 +301,8 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
   const int shtiles = A.Is > 0 ? (A.T + BM - 1) / BM : 0;
   const int ntl = MODE == 2 ? 0 : *L.ntiles - (part == 1 ? shtiles : 0);
   const int nreal = MODE == 2 || part == 2 ? nblocks : min(nblocks, ntl * nb_per_tile);
-  if ((int)blockIdx.x >= nreal) return;
-  const int b = xcd_swizzle(blockIdx.x, nreal);
+  if (bid >= nreal) return;
+  const int b = xcd_swizzle(bid, nreal);
   const int tb = b / nb_per_tile, ti = tb + (part == 2 ? *L.ntiles - shtiles : 0);
   int nb = b - tb * nb_per_tile, ksp = 0;  // router: nb_per_tile counts (group, K split) pairs
   if constexpr (MODE == 2) {
@@ -652,6 +653,12 @@ void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
   }
 }
 
+template <int MODE, int BM, int NS, int WT, bool P>
+__global__ __launch_bounds__(2 * BM, BM == 128 ? (NS == 2 ? 3 : 2) : 1)
+void pf_gemm(Args A, PfLayout L, int nb_per_tile, int nblocks, int part) {
+  pf_gemm_body<MODE, BM, NS, WT, P>(A, L, nb_per_tile, nblocks, part, blockIdx.x);
+}
+
 // ------------------------------------------------------------------------------------------
 // W4A8: MXFP8 activations against MXFP4 weights on gfx950's block-scaled matrix cores
 // ("Three ways to boost mixture-of-experts inference on NVIDIA DGX Spark", section "Why
@@ -719,8 +726,8 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 // MODE 0 gate/up: A = the tile's token rows of xq, epilogue SwiGLU -> MXFP8 activations (aq, as).
 // MODE 1 down: A = the tile's rows of aq; epilogue: fp32 rows weighted by the routing weight.
 template <int MODE, int NS>
-__global__ __launch_bounds__(2 * kPfBM, 2) void pf_gemm_w4a8(Args A, PfLayout L, int nb_per_tile, int nblocks,
-                                                               int /*part: the routed tiles only*/) {
+__device__ __forceinline__ void pf_gemm_w4a8_body(const Args& A, const PfLayout& L, int nb_per_tile, int nblocks,
+                                                  int bid) {  // the routed tiles only
   constexpr int BM = kPfBM;
   constexpr int kUA = BM * 64 / 16;        // 16-byte units of A per stage (128 rows x 64 bytes)
   constexpr int kUB = kPfBN * 32 / 16;     // of B (256 rows x 32 bytes)
@@ -732,8 +739,8 @@ __global__ __launch_bounds__(2 * kPfBM, 2) void pf_gemm_w4a8(Args A, PfLayout L,
   const int shtiles = A.Is > 0 ? (A.T + BM - 1) / BM : 0;
   const int ntl = *L.ntiles - shtiles;  // the routed groups' tiles come first in the map
   const int nreal = min(nblocks, ntl * nb_per_tile);
-  if ((int)blockIdx.x >= nreal) return;
-  const int b = xcd_swizzle(blockIdx.x, nreal);
+  if (bid >= nreal) return;
+  const int b = xcd_swizzle(bid, nreal);
   const int ti = b / nb_per_tile, nb = b - ti * nb_per_tile;
   const int4 tl = ((const int4*)L.tiles)[ti];  // {group, first row, rows, 0}
   const int g = tl.x, pos0 = tl.y, nrows = tl.z;
@@ -935,6 +942,31 @@ __global__ __launch_bounds__(2 * kPfBM, 2) void pf_gemm_w4a8(Args A, PfLayout L,
   (void)S;
 }
 
+template <int MODE, int NS>
+__global__ __launch_bounds__(2 * kPfBM, 2) void pf_gemm_w4a8(Args A, PfLayout L, int nb_per_tile, int nblocks, int) {
+  pf_gemm_w4a8_body<MODE, NS>(A, L, nb_per_tile, nblocks, blockIdx.x);
+}
+
+// One launch for the two kinds of tile of a layer with 4-bit experts: the shared expert's
+// (bf16, precise) tiles take the first nblk_s blocks, the routed groups' tiles (WT; MOE_MXFP4
+// with W8 = W4A8) the rest.  The shared tiles then share the machine with the routed ones
+// instead of running alone at low occupancy after them.  The shared down tiles keep a
+// two-stage ring, so that their LDS (bf16 weight rows and two activation parts per stage) stays
+// within the routed tiles' and two blocks fit per CU.
+template <int MODE>
+constexpr int kMixNsShared = MODE == 1 ? kPfNSG : kPfNS;
+template <int MODE, int WT, bool W8>
+__global__ __launch_bounds__(2 * kPfBM, 2) void pf_gemm_mix(Args A, PfLayout L, int nbt_s, int nblk_s, int nbt_r,
+                                                             int nblk_r) {
+  if ((int)blockIdx.x < nblk_s) {
+    pf_gemm_body<MODE, kPfBM, kMixNsShared<MODE>, MOE_BF16, true>(A, L, nbt_s, nblk_s, 2, blockIdx.x);
+  } else if constexpr (W8) {
+    pf_gemm_w4a8_body<MODE, kPfNS>(A, L, nbt_r, nblk_r, (int)blockIdx.x - nblk_s);
+  } else {
+    pf_gemm_body<MODE, kPfBM, kPfNS, WT, true>(A, L, nbt_r, nblk_r, 1, (int)blockIdx.x - nblk_s);
+  }
+}
+
 __global__ __launch_bounds__(256) void pf_select(Args A, const float* rpart, int ks) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -1064,59 +1096,50 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   // INT4G64 experts: the routed tiles run the int4 kernel (weights rebuilt in bf16 on the way
   // into the MFMA), the shared tiles the bf16 kernel, both precise as for MXFP4.  The weights'
   // own bf16 rounding stays (the page's reconstruction); the activations and slot rows keep
-  // about 16 significant bits, so those roundings do not add to it.
+  // about 16 significant bits, so those roundings do not add to it.  W4A8: the routed tiles run
+  // the block-scaled fp8 x fp4 kernel, the shared tiles the bf16 precise kernel.  With 4-bit
+  // experts both kinds of tile go into one launch (pf_gemm_mix: shared tiles first).
+  const int shtiles = A.Is > 0 ? (A.T + kPfBM - 1) / kPfBM : 0;
   auto run = [&](const char* name, const void* f, int nblocks, int nbt, int part, size_t lds) -> int {
     PfLayout Lc = L;
     void* args[] = {&A, &Lc, &nbt, &nblocks, &part};
     return launch(hook, name, f, dim3(nblocks), dim3(2 * kPfBM), args, lds, st) == hipSuccess ? MOE_OK : MOE_EHIP;
   };
-  const int shtiles = A.Is > 0 ? (A.T + kPfBM - 1) / kPfBM : 0;
+  auto run_mix = [&](const char* name, const void* f, int nbt, size_t lds) -> int {
+    PfLayout Lc = L;
+    int nbs = nbt, nblk_s = shtiles * nbt, nbr = nbt, nblk_r = cap * nbt;
+    void* args[] = {&A, &Lc, &nbs, &nblk_s, &nbr, &nblk_r};
+    return launch(hook, name, f, dim3(nblk_s + nblk_r), dim3(2 * kPfBM), args, lds, st) == hipSuccess ? MOE_OK
+                                                                                                     : MOE_EHIP;
+  };
   {
     const int nbt = (Imax + kPfBN / 2 - 1) / (kPfBN / 2);
-    if (w4a8) {
-      rc = run("pf_gateup", (const void*)pf_gemm_w4a8<0, kPfNS>, cap * nbt, nbt, 1, w4a8_lds(A.H));
-      if (!rc && shtiles)
-        rc = run("pf_gateup_shared", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, true>, shtiles * nbt, nbt, 2,
-                 pf_lds<0, kPfNS, MOE_BF16, true>(A.H));
-    } else if (i4) {
-      rc = run("pf_gateup", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_INT4G64, true>, cap * nbt, nbt, 1,
-               pf_lds<0, kPfNS, MOE_INT4G64, true>(A.H));
-      if (!rc && shtiles)
-        rc = run("pf_gateup_shared", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, true>, shtiles * nbt, nbt, 2,
-                 pf_lds<0, kPfNS, MOE_BF16, true>(A.H));
-    } else if (!f4) {
+    const size_t lsh = pf_lds<0, kMixNsShared<0>, MOE_BF16, true>(A.H);
+    if (w4a8)
+      rc = run_mix("pf_gateup", (const void*)pf_gemm_mix<0, MOE_MXFP4, true>, nbt, std::max(w4a8_lds(A.H), lsh));
+    else if (i4)
+      rc = run_mix("pf_gateup", (const void*)pf_gemm_mix<0, MOE_INT4G64, false>, nbt,
+                   std::max(pf_lds<0, kPfNS, MOE_INT4G64, true>(A.H), lsh));
+    else if (f4)
+      rc = run_mix("pf_gateup", (const void*)pf_gemm_mix<0, MOE_MXFP4, false>, nbt,
+                   std::max(pf_lds<0, kPfNS, MOE_MXFP4, true>(A.H), lsh));
+    else
       rc = run("pf_gateup", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, false>, cap * nbt, nbt, 0, 0);
-    } else {
-      rc = run("pf_gateup", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_MXFP4, true>, cap * nbt, nbt, 1,
-               pf_lds<0, kPfNS, MOE_MXFP4, true>(A.H));
-      if (!rc && shtiles)
-        rc = run("pf_gateup_shared", (const void*)pf_gemm<0, kPfBM, kPfNS, MOE_BF16, true>, shtiles * nbt, nbt, 2,
-                 pf_lds<0, kPfNS, MOE_BF16, true>(A.H));
-    }
     if (rc) return rc;
   }
   {
     const int nbt = (A.H + kPfBN - 1) / kPfBN;
-    if (w4a8) {
-      rc = run("pf_down", (const void*)pf_gemm_w4a8<1, kPfNS>, cap * nbt, nbt, 1, w4a8_lds(A.I));
-      if (!rc && shtiles)
-        rc = run("pf_down_shared", (const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, true>, shtiles * nbt, nbt, 2,
-                 pf_lds<1, kPfNSG, MOE_BF16, true>(A.Is));
-    } else if (i4) {
-      rc = run("pf_down", (const void*)pf_gemm<1, kPfBM, kPfNS, MOE_INT4G64, true>, cap * nbt, nbt, 1,
-               pf_lds<1, kPfNS, MOE_INT4G64, true>(A.I));
-      if (!rc && shtiles)
-        rc = run("pf_down_shared", (const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, true>, shtiles * nbt, nbt, 2,
-                 pf_lds<1, kPfNSG, MOE_BF16, true>(A.Is));
-    } else if (!f4) {
+    const size_t lsh = pf_lds<1, kMixNsShared<1>, MOE_BF16, true>(A.Is);
+    if (w4a8)
+      rc = run_mix("pf_down", (const void*)pf_gemm_mix<1, MOE_MXFP4, true>, nbt, std::max(w4a8_lds(A.I), lsh));
+    else if (i4)
+      rc = run_mix("pf_down", (const void*)pf_gemm_mix<1, MOE_INT4G64, false>, nbt,
+                   std::max(pf_lds<1, kPfNS, MOE_INT4G64, true>(A.I), lsh));
+    else if (f4)
+      rc = run_mix("pf_down", (const void*)pf_gemm_mix<1, MOE_MXFP4, false>, nbt,
+                   std::max(pf_lds<1, kPfNS, MOE_MXFP4, true>(A.I), lsh));
+    else
       rc = run("pf_down", (const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, false>, cap * nbt, nbt, 0, 0);
-    } else {
-      rc = run("pf_down", (const void*)pf_gemm<1, kPfBM, kPfNS, MOE_MXFP4, true>, cap * nbt, nbt, 1,
-               pf_lds<1, kPfNS, MOE_MXFP4, true>(A.I));
-      if (!rc && shtiles)
-        rc = run("pf_down_shared", (const void*)pf_gemm<1, kPfBM, kPfNSG, MOE_BF16, true>, shtiles * nbt, nbt, 2,
-                 pf_lds<1, kPfNSG, MOE_BF16, true>(A.Is));
-    }
     if (rc) return rc;
   }
   void* ac[] = {&A, &L};

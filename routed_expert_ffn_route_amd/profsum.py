@@ -32,15 +32,14 @@ KERNEL_SOURCES = {
     "pf_": ["csrc/prefill.hip", "csrc/route.hip", "csrc/select.h", "csrc/common.h", "csrc/kernels.h"],
 }
 # bench label -> regular expression over the demangled kernel name rocprofv3 reports
-# (pf_gemm<MODE, BM, NS, weight dtype, precise>; dtype 1 = bf16, 2 = MXFP4, 3 = int4; pf_gemm_w4a8<MODE, NS>)
+# (pf_gemm<MODE, BM, NS, weight dtype, precise>: the bf16 layer; pf_gemm_mix<MODE, weight dtype, W4A8>:
+# the 4-bit layers, shared and routed tiles in one launch)
 KERNEL_SYMBOLS = {
     "dec_router": r"dec_router<", "dec_select": r"dec_select<", "dec_gateup": r"dec_gateup<",
     "dec_down": r"dec_down<",
     "pf_router_split": r"pf_split_router\(", "pf_router": r"pf_gemm<2, ",
-    "pf_gateup": r"pf_gemm<0, \d+, \d+, (1, false|2, true|3, true)>|pf_gemm_w4a8<0,",
-    "pf_gateup_shared": r"pf_gemm<0, \d+, \d+, 1, true>",
-    "pf_down": r"pf_gemm<1, \d+, \d+, (1, false|2, true|3, true)>|pf_gemm_w4a8<1,",
-    "pf_down_shared": r"pf_gemm<1, \d+, \d+, 1, true>", "pf_quant_x": r"pf_quant_x\(",
+    "pf_gateup": r"pf_gemm<0, \d+, \d+, 1, false>|pf_gemm_mix<0,",
+    "pf_down": r"pf_gemm<1, \d+, \d+, 1, false>|pf_gemm_mix<1,", "pf_quant_x": r"pf_quant_x\(",
     "pf_select": r"pf_select\(", "pf_combine": r"pf_combine\(",
 }
 

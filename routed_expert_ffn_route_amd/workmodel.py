@@ -90,7 +90,7 @@ def kernel_work(spec, distinct):
     sh_gu, sh_dn = 2 * Is * H * ss, Is * H * ss
     S = T * k                                  # routed rows (slots); the shared expert adds T rows
     # MXFP4 and int4 prefill run the precise kernels: activations as bf16 hi + lo (4 B per value), fp32
-    # slot rows, and the shared expert's tiles in launches of their own
+    # slot rows; the shared expert's tiles run in the same launches (bf16, precise)
     p = spec["expert"] in ("mxfp4", "int4g64")
     ab, rb = (4, 4) if p else (2, 2)           # bytes per activation value, per slot-row value
     w = {
@@ -105,22 +105,25 @@ def kernel_work(spec, distinct):
         "pf_router_split": ("hbm", E * H * 4 + 3 * E * H * 2, 0.0),
         # (the fp32 router runs as three bf16 parts, three times the MFMA work of its 2 T E H)
         "pf_router": ("mfma", 3 * E * H * 2 + T * H * 2 + T * E * 4, 2.0 * T * E * H),
-        "pf_gateup": ("mfma", distinct * gu + T * H * 2 + S * I * ab + (0 if p else sh_gu + T * Is * ab),
-                      4.0 * S * I * H + (0.0 if p else 4.0 * T * Is * H)),
-        "pf_gateup_shared": ("mfma", sh_gu + T * H * 2 + T * Is * ab, 4.0 * T * Is * H),
-        "pf_down": ("mfma", distinct * dn + S * (I * ab + H * rb) + (0 if p else sh_dn + T * (Is * ab + H * rb)),
-                    2.0 * S * I * H + (0.0 if p else 2.0 * T * Is * H)),
-        "pf_down_shared": ("mfma", sh_dn + T * (Is * ab + H * rb), 2.0 * T * Is * H),
+        "pf_gateup": ("mfma", distinct * gu + sh_gu + T * H * 2 + (S * I + T * Is) * ab, 4.0 * (S * I + T * Is) * H),
+        "pf_down": ("mfma", distinct * dn + sh_dn + S * (I * ab + H * rb) + T * (Is * ab + H * rb),
+                    2.0 * (S * I + T * Is) * H),
         "pf_combine": ("hbm", (S + T) * H * rb + T * H * ys, 0.0),
     }
-    if spec.get("act_quant") == "mxfp8":   # W4A8: 1-byte activations + a scale byte per 32
+    w8 = spec.get("act_quant") == "mxfp8"
+    if w8:   # W4A8: 1-byte activations + a scale byte per 32 on the routed tiles; shared tiles as bf16 precise
         xq = T * H + T * H // 32
         w["pf_quant_x"] = ("hbm", T * H * 2 + xq, 0.0)
-        w["pf_gateup"] = ("mfma", distinct * gu + xq + S * I + S * I // 32, 4.0 * S * I * H)
-        w["pf_down"] = ("mfma", distinct * dn + S * I + S * I // 32 + S * H * rb, 2.0 * S * I * H)
+        w["pf_gateup"] = ("mfma", distinct * gu + xq + S * I + S * I // 32 + sh_gu + T * H * 2 + T * Is * ab,
+                          4.0 * (S * I + T * Is) * H)
+        w["pf_down"] = ("mfma", distinct * dn + S * I + S * I // 32 + S * H * rb + sh_dn + T * (Is * ab + H * rb),
+                        2.0 * (S * I + T * Is) * H)
     out = {n: {"bound": b, "bytes": int(by), "flops": float(f)} for n, (b, by, f) in w.items()}
     for n, v in out.items():   # the matrix-core peak each GEMM is measured against
         if v["bound"] == "mfma":
-            v["peak_tflops"] = (FP8_MFMA_PEAK_TFLOPS if spec.get("act_quant") == "mxfp8" and n in ("pf_gateup", "pf_down")
-                                else BF16_MFMA_PEAK_TFLOPS)
+            v["peak_tflops"] = BF16_MFMA_PEAK_TFLOPS
+    if w8:   # routed flops at the fp8 x fp4 rate, shared at the bf16 rate: the peak of the mix
+        for n, share in (("pf_gateup", 4.0 * T * Is * H), ("pf_down", 2.0 * T * Is * H)):
+            f = out[n]["flops"]
+            out[n]["peak_tflops"] = round(f / ((f - share) / FP8_MFMA_PEAK_TFLOPS + share / BF16_MFMA_PEAK_TFLOPS), 1)
     return out
