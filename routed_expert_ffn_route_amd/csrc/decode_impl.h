@@ -545,9 +545,10 @@ __device__ __forceinline__ void shared_gateup_block(const Args& A, int blk, int 
 
 // Selection and the decode plan (T > 1): the last block; wave t selects token t (select_set:
 // the k largest logits, ties to the lower index, renormalised softmax weights), then the
-// distinct experts are compacted in ascending id with one ballot per 64 experts.  The
-// blocks before it compute the shared expert's gate/up (shared_gateup_block), which keeps HBM
-// busy while the selection runs.  Block size 64 * TM (TM >= T).
+// distinct experts are compacted in ascending id with one ballot per 64 experts.  The nsh
+// blocks before it (none when the gate/up kernel takes the shared expert) compute the shared
+// expert's gate/up (shared_gateup_block), which keeps HBM busy while the selection runs.
+// Block size 64 * TM (TM >= T).
 template <int XT, int SWT, int TM, bool XL>
 __global__ __launch_bounds__(kWave * TM) void dec_select(Args A, int nsh) {
   extern __shared__ uint4 s_xs[];
@@ -1105,9 +1106,11 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   // 4-bit experts read x from padded LDS rows (16 bytes after every 64)
   constexpr bool w4 = WT == MOE_MXFP4 || WT == MOE_INT4G64;
   const size_t xbytes_gu = w4 ? xbytes / 4 * 5 : xbytes;
-  // shared expert gate/up: one row per wave, in the selection kernel (T > 1) or beside the
-  // routed rows of the gate/up kernel (T = 1)
-  const int sh_waves = TM == 1 ? kWaves : TM;
+  // shared expert gate/up: one row per wave, in the selection kernel's blocks (T = 2..8) or
+  // beside the routed rows of the gate/up kernel (T = 1, and T > 8, where the selection
+  // kernel's 16-wave blocks would be too few to stream it)
+  constexpr bool sh_in_sel = TM > 1 && TM <= 8;
+  const int sh_waves = sh_in_sel ? TM : kWaves;
   int nsh = A.Is > 0 ? (A.Is + sh_waves - 1) / sh_waves : 0;
   void* args1[] = {&A};
   hipError_t err = launch(hook, "dec_router", router_fn<XT>(A.T), dim3(A.E), dim3(kThreads), args1, 0, st);
@@ -1115,16 +1118,18 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   if (route_only) return MOE_OK;
   if (TM > 1) {
     void* fs = xl ? (void*)dec_select<XT, SWT, TM, true> : (void*)dec_select<XT, SWT, TM, false>;
-    void* args_s[] = {&A, &nsh};
-    err = launch(hook, "dec_select", fs, dim3(nsh + 1), dim3(kWave * TM), args_s, xl ? xbytes : 0, st);
+    int nsel = sh_in_sel ? nsh : 0;
+    void* args_s[] = {&A, &nsel};
+    err = launch(hook, "dec_select", fs, dim3(nsel + 1), dim3(kWave * TM), args_s, xl ? xbytes : 0, st);
     if (err != hipSuccess) return MOE_EHIP;
   }
 
-  // gate/up: (T = 1: shared gate/up blocks first, then) (distinct expert, row tile) blocks
+  // gate/up: (shared gate/up blocks first unless the selection kernel has them, then)
+  // (distinct expert, row tile) blocks
   const int g2 = TM == 1 ? pick_gn(kGU1, A.H / gu_epc(WT)) : pick_gn(kGUn, A.H / gu_epc(WT));
   const int rb2 = kWaves * (kWave / GUL[g2].G);
   int tiles = (A.I + rb2 - 1) / rb2;
-  int sh_blocks = TM == 1 ? nsh : 0;
+  int sh_blocks = sh_in_sel ? 0 : nsh;
   void* f2;
   if constexpr (TM == 1)
     f2 = gateup_fn<XT, WT, SWT, TM, GUL, true, true>(g2);

@@ -326,6 +326,8 @@ def test_route_end_to_end(orc, B, T, H, E, k, bias):
     dict(T=4, H=4608, E=16, k=2, I=64, I_shared=64),           # row longer than one slice
     dict(T=16, H=4096, E=32, k=4, I=128, I_shared=64),         # x (128 KiB) too large for LDS
     dict(T=7, H=5120, E=24, k=3, I=96, I_shared=32),           # token tile 8, x from global
+    dict(T=12, H=2048, E=256, k=8, I=512, I_shared=512),       # token tile 16 at Qwen shapes:
+                                                               # shared gate/up in the gate/up kernel
 ])
 def test_decode_edge_shapes_bf16(orc, B, kw):
     say(f"[decode-edge] {kw}")
