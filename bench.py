@@ -242,6 +242,27 @@ def main():
         layer["read_ceiling_gbs"] = ceil_gbs
         layer["frac_of_read_ceiling"] = round(layer["gbs"] / ceil_gbs, 4)
         del big, gc
+    else:
+        # operand-staging rates of the grouped GEMMs' load into LDS, by contiguous bytes per row
+        # (4-bit weight rows: 16 per step; bf16 operand rows: 64; whole cache lines: 128), from a
+        # 2 MiB region that stays in the L2
+        reg = torch.empty(2 << 20, dtype=torch.uint8, device="cuda")
+        reg.fill_(1)
+        sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+        rates = {}
+        for seg in (16, 64, 128):
+            for _ in range(2):
+                nb = B.stage_rate(reg, 2 << 20, seg, 256, sink, stream.cuda_stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                B.stage_rate(reg, 2 << 20, seg, 256, sink, stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gbs = 5 * nb / (e0.elapsed_time(e1) / 1e3) / 1e9
+            rates[str(seg)] = {"gbs": round(gbs, 1), "bytes_per_clk_per_cu": round(gbs * 1e9 / 256 / 2.4e9, 1)}
+        layer["stage_rate"] = rates
+        del reg
 
     # ---- roofline of the dominant kernel ----
     roof = None

@@ -259,6 +259,26 @@ int moe_timing_end(moe_kernel_time_t *out, int32_t max_out, int32_t *n_out);
  */
 int moe_read_ceiling(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
+/*
+ * Operand-staging probe for measurement: the prefill GEMMs' way of feeding
+ * their matrix cores (16 bytes per lane loaded from memory straight into LDS)
+ * with each load instruction covering rows of seg_bytes contiguous bytes, rows
+ * 4 KiB apart inside the first region_bytes of buf.  512 blocks of four
+ * waves; each wave moves iters * 6144 bytes with six loads in flight, so one
+ * call moves 512 * 4 * iters * 6144 bytes.  Timing it for seg_bytes 16, 64 and
+ * 128 over a region that fits the L2 gives the rate at which the 4-bit weight
+ * rows (16 bytes per 32-deep step), the bf16 operand rows (64) and full cache
+ * lines (128) can be staged ("Optimizing on-device inference for Apple
+ * Silicon", section "Limits of further optimization": kernels are compared
+ * with the fastest rate their access pattern sustains).  region_bytes a power
+ * of two in [8 KiB, 2 GiB], seg_bytes a power of two in [16, 1024], iters >= 1,
+ * null pointers: MOE_EINVAL; buf not 16-byte or sink not 4-byte aligned:
+ * MOE_EALIGN.  sink: 64 writable uint32 of device memory (in practice not
+ * written).
+ */
+int moe_stage_rate(const void *buf, size_t region_bytes, int32_t seg_bytes, int32_t iters, uint32_t *sink,
+                   void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,7 +15,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP, MOE_
 STATIC_SCRATCH_BYTES = 32 << 20   # MOE_STATIC_SCRATCH_BYTES
 DTYPES = {"f32": 0, "bf16": 1, "mxfp4": 2, "int4g64": 3}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_static", "moe_workspace_routing",
-           "moe_path_name", "moe_strerror", "moe_timing_begin", "moe_timing_end", "moe_read_ceiling")
+           "moe_path_name", "moe_strerror", "moe_timing_begin", "moe_timing_end", "moe_read_ceiling",
+           "moe_stage_rate")
 
 
 class Shape(ctypes.Structure):
@@ -77,8 +78,9 @@ def lib():
         L.moe_timing_end.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32,
                                      ctypes.POINTER(ctypes.c_int32)]
         L.moe_read_ceiling.argtypes = [P, ctypes.c_size_t, P, P]
+        L.moe_stage_rate.argtypes = [P, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, P, P]
         for n in ("moe_workspace_size", "moe_route", "moe_forward", "moe_forward_static", "moe_workspace_routing",
-                  "moe_timing_begin", "moe_timing_end", "moe_read_ceiling"):
+                  "moe_timing_begin", "moe_timing_end", "moe_read_ceiling", "moe_stage_rate"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -197,6 +199,14 @@ def read_ceiling(buf, nbytes: int, sink, stream=None) -> None:
     rc = lib().moe_read_ceiling(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
     if rc:
         raise MoeError(rc, "moe_read_ceiling")
+
+
+def stage_rate(buf, region_bytes: int, seg_bytes: int, iters: int, sink, stream=None) -> int:
+    """moe_stage_rate: the operand-staging probe; returns the bytes one call moves."""
+    rc = lib().moe_stage_rate(_ptr(buf), region_bytes, seg_bytes, iters, _ptr(sink), _stream(stream))
+    if rc:
+        raise MoeError(rc, "moe_stage_rate")
+    return 512 * 4 * iters * 6144
 
 
 # Convenience on a synth.Layer of device tensors --------------------------------------------

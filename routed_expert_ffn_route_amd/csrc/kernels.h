@@ -51,6 +51,12 @@ int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook);
 // Prefill path (T > kDecodeMaxT): grouped GEMMs on MFMA.
 int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook);
 
+// Operand-staging probe (measurement): kStageProbeBlocks blocks of four waves, each wave
+// moving iters * 6 KiB from a region of mask + 1 bytes (a power of two >= 8 KiB) into LDS in
+// rows of seg bytes (16 .. 1024, a power of two).
+constexpr int kStageProbeBlocks = 512;
+int launch_stage_probe(const void* buf, uint32_t mask, int seg, int iters, uint32_t* sink, hipStream_t st);
+
 // Workspace bytes needed by the prefill path's sections; precise: MXFP4 or INT4G64 experts
 // (activations as bf16 hi + lo parts, fp32 slot rows).
 size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is, bool precise, bool w4a8);

@@ -48,3 +48,13 @@ extern "C" int moe_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, v
              ? MOE_OK
              : MOE_EHIP;
 }
+
+extern "C" int moe_stage_rate(const void* buf, size_t region_bytes, int32_t seg_bytes, int32_t iters, uint32_t* sink,
+                              void* stream) {
+  using namespace moe;
+  if (!buf || !sink || iters < 1) return MOE_EINVAL;
+  if (region_bytes < 8192 || region_bytes > ((size_t)1 << 31) || (region_bytes & (region_bytes - 1))) return MOE_EINVAL;
+  if (seg_bytes < 16 || seg_bytes > 1024 || (seg_bytes & (seg_bytes - 1))) return MOE_EINVAL;
+  if (((uintptr_t)buf & 15u) || ((uintptr_t)sink & 3u)) return MOE_EALIGN;
+  return launch_stage_probe(buf, (uint32_t)(region_bytes - 1), seg_bytes, iters, sink, (hipStream_t)stream);
+}

@@ -1035,6 +1035,56 @@ __global__ __launch_bounds__(256) void pf_combine(Args A, PfLayout L) {
 
 }  // namespace
 
+namespace {
+// Operand-staging probe: the grouped GEMMs' load (16 bytes per lane from a buffer resource
+// into LDS) with each instruction covering 64 * 16 / SEG rows of SEG contiguous bytes, rows
+// 4 KiB apart in a region of mask + 1 bytes.  Every wave issues `iters` groups of six
+// instructions and keeps six in flight; what lands is folded into a test that stores to sink
+// only for a value no sane input produces.  Every offset stays inside the region: a row starts
+// on a 4 KiB boundary below it and the segment ends within 2 KiB of that start.
+template <int SEG>
+__global__ __launch_bounds__(256) void stage_probe(const uint8_t* buf, uint32_t mask, int iters, uint32_t* sink) {
+  __shared__ __attribute__((aligned(16))) uint4 s[2][4][6][64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const i32x4_t rs = buf_rsrc(buf, (size_t)mask + 1);
+  constexpr int LPR = SEG / 16, RPI = 64 / LPR;  // lanes per row, rows per instruction
+  const uint32_t lr = (uint32_t)(lane / LPR), within = (uint32_t)(lane % LPR) * 16u;
+  const uint32_t row0 = (uint32_t)(blockIdx.x * 4 + wave) * 37u;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const uint32_t g = (uint32_t)(it * 6 + j);
+      const uint32_t seg0 = SEG >= 1024 ? 0u : (g * SEG) & 1023u;
+      const uint32_t off = ((row0 + g * RPI + lr) * 4096u & mask & ~4095u) + seg0 + within;
+      dma16(rs, off, lds_addr(&s[it & 1][wave][j][0]));
+    }
+    wait_vm<6>();
+  }
+  wait_vm<0>();
+  __syncthreads();
+  if (s[0][wave][0][lane].x == 0x9E3779B9u) sink[blockIdx.x & 63] = 1u;
+}
+}  // namespace
+
+int launch_stage_probe(const void* buf, uint32_t mask, int seg, int iters, uint32_t* sink, hipStream_t st) {
+  const void* f = nullptr;
+  switch (seg) {
+    case 16: f = (const void*)stage_probe<16>; break;
+    case 32: f = (const void*)stage_probe<32>; break;
+    case 64: f = (const void*)stage_probe<64>; break;
+    case 128: f = (const void*)stage_probe<128>; break;
+    case 256: f = (const void*)stage_probe<256>; break;
+    case 512: f = (const void*)stage_probe<512>; break;
+    case 1024: f = (const void*)stage_probe<1024>; break;
+    default: return MOE_EINVAL;
+  }
+  const uint8_t* b = (const uint8_t*)buf;
+  void* args[] = {&b, &mask, &iters, &sink};
+  return launch(LaunchHook{}, "stage_probe", f, dim3(kStageProbeBlocks), dim3(256), args, 0, st) == hipSuccess
+             ? MOE_OK
+             : MOE_EHIP;
+}
+
 // Router logits + per-token selection for T > 16 with bf16 activations (also used by
 // moe_route so that routing-only calls take the forward path's arithmetic).
 int launch_pf_route(Args A, hipStream_t st, const LaunchHook& hook) {

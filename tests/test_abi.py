@@ -203,6 +203,17 @@ def test_read_ceiling_validates_arguments(lib):
     assert L.moe_read_ceiling(0x1008, 1024, 0x2000, None) == B.MOE_EALIGN
 
 
+def test_stage_rate_validates_arguments(lib):
+    L = B.lib()
+    ok = (0x1000, 1 << 21, 64, 4, 0x2000, None)
+    for i, bad in [(0, None), (1, 4096), (1, 3 << 20), (2, 8), (2, 48), (2, 2048), (3, 0), (4, None)]:
+        a = list(ok)
+        a[i] = bad
+        assert L.moe_stage_rate(*a) == B.MOE_EINVAL, (i, bad)
+    assert L.moe_stage_rate(0x1008, 1 << 21, 64, 4, 0x2000, None) == B.MOE_EALIGN
+    assert L.moe_stage_rate(0x1000, 1 << 21, 64, 4, 0x2002, None) == B.MOE_EALIGN
+
+
 def test_timing_api_rejects_misuse(lib):
     assert B.lib().moe_timing_begin(0) == B.MOE_EINVAL
     n = ctypes.c_int32(0)

@@ -687,3 +687,17 @@ def test_ling_w4a8_prefill_full_size(orc, B):
     Ld, xd = synth.device_layer(4096, 2560, 512, 8, 768, 768, "bf16", "mxfp4", "bf16", "f32", seed=5, bias="zipf")
     Ld = dataclasses.replace(Ld, act_quant="mxfp8")
     prefill_full_size_check(orc, B, Ld, xd, "w4a8-prefill-4096", nrand=16, seed=3)
+
+
+@pytest.mark.gpu
+def test_stage_rate_probe_runs_and_writes_nothing(B):
+    """The operand-staging probe launches for every row-segment size and leaves sink alone."""
+    import torch
+    say("[stage-rate] segments 16..1024")
+    reg = torch.ones(1 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    for seg in (16, 32, 64, 128, 256, 512, 1024):
+        assert B.stage_rate(reg, 1 << 20, seg, 3, sink) == 512 * 4 * 3 * 6144
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+
