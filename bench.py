@@ -102,7 +102,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="qwen_decode")
     ap.add_argument("--T", type=int, default=None)
-    ap.add_argument("--d", type=int, default=32)
+    ap.add_argument("--d", type=int, default=None, help="distinct experts of a verify window (default min(32, 8 T))")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

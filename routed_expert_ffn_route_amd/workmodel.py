@@ -17,18 +17,22 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
 FP8_MFMA_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 matrix cores (the W4A8 GEMMs' fp8 x fp4 rate)
 
 
-def workload_spec(name, T_override=None, d=32):
-    """Shapes and dtypes of the benchmark workloads (seeded synthetic inputs, see synth.py)."""
+def workload_spec(name, T_override=None, d=None):
+    """Shapes and dtypes of the benchmark workloads (seeded synthetic inputs, see synth.py).
+    d: distinct experts of a verify window (default 32, at most T * k)."""
+    def window(T):
+        return d if d is not None else min(32, T * 8)
     if name == "qwen_decode":
         return dict(T=T_override or 1, H=2048, E=256, k=8, I=512, I_shared=512, act="bf16", expert="bf16",
                     shared="bf16", out="bf16", bias=None, d=None, layers=48)
     if name == "ling_verify":
-        return dict(T=T_override or 4, H=2560, E=512, k=8, I=768, I_shared=768, act="bf16", expert="bf16",
-                    shared="bf16", out="bf16", bias="verify", d=d, layers=8)
+        T = T_override or 4
+        return dict(T=T, H=2560, E=512, k=8, I=768, I_shared=768, act="bf16", expert="bf16",
+                    shared="bf16", out="bf16", bias="verify", d=window(T), layers=8)
     if name == "ling_mxfp4":
         T = T_override or 1
         return dict(T=T, H=2560, E=512, k=8, I=768, I_shared=768, act="bf16", expert="mxfp4",
-                    shared="bf16", out="f32", bias=("verify" if T > 1 else None), d=(d if T > 1 else None),
+                    shared="bf16", out="f32", bias=("verify" if T > 1 else None), d=(window(T) if T > 1 else None),
                     layers=48)
     if name == "ling_mxfp4_prefill":
         return dict(T=T_override or 4096, H=2560, E=512, k=8, I=768, I_shared=768, act="bf16", expert="mxfp4",
