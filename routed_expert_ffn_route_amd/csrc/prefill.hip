@@ -421,6 +421,20 @@ __device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, i
   const int nk_all = K / kPfBK;
   const int s0 = MODE == 2 ? ksp * nk_all / L.ks : 0;
   const int nk = MODE == 2 ? (ksp + 1) * nk_all / L.ks - s0 : nk_all;
+  constexpr int kNL = kNA + kNB;  // load instructions per wave per step
+  // load li of step st (A, then the precise A's lo parts, then B) into its stage
+  auto issue_one = [&](int st, uint4* stage, int li) {
+    const uint32_t ks = (uint32_t)(s0 + (st < nk ? st : nk - 1));
+    const uint32_t kb = ks * kPfBK * 2u, kbb = F4 ? ks * 16u : kb;
+    if (li < 2) {
+      dma16(ra, ao[li] + kb, lds_addr(stage + (wave * 2 + li) * 64));
+    } else if (C::AHL && li < 4) {
+      dma16(ra_lo, ao[li - 2] + kb, lds_addr(stage + C::kUnitsA + (wave * 2 + li - 2) * 64));
+    } else {
+      const int j = li - (C::AHL ? 4 : 2);
+      dma16(rb[j], bo[j] + kbb, lds_addr(stage + kStageA + (wave * kNB + j) * 64));
+    }
+  };
   auto issue = [&](int st, uint4* stage) {
     const uint32_t ks = (uint32_t)(s0 + (st < nk ? st : nk - 1));
     const uint32_t kb = ks * kPfBK * 2u, kbb = F4 ? ks * 16u : kb;
@@ -467,14 +481,20 @@ __device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, i
   f32x16_t acc[2][4] = {};
   // One K-step: wait for its stage, refill the ring, then the fragment reads of the step (both
   // 16-deep halves, or one half at a time with a two-stage ring) before their MFMAs, so that
-  // the reads' latency overlaps the first MFMAs.  ML = the wave's live 32-row groups, a constant inside the loop (the loop is
+  // the reads' latency overlaps the first MFMAs.  The precise down GEMM (two MFMAs per tile)
+  // issues the refill loads one at a time between its MFMAs instead: a load waits in the
+  // buffer unit's queue while the MFMAs issued before it run (its precise 4-bit downs measured
+  // 4-5% faster that way; the one-MFMA GEMMs are slower with it).  ML = the wave's live 32-row groups, a constant inside the loop (the loop is
   // instantiated per value), so nothing branches between the MFMAs.
   auto step = [&](auto ml_c, int s) {
     constexpr int ML = decltype(ml_c)::value;
     wait_vm<(kNA + kNB) * (NS - 2)>();  // this wave's loads of step s have landed (later ones in flight)
     __syncthreads();          // ... and every other wave's; all are done with step s - 1's stage
-    issue(s + NS - 1, smem + ((s + NS - 1) % NS) * kStage);
+    uint4* const nst = smem + ((s + NS - 1) % NS) * kStage;
+    constexpr bool kSpread = C::AHL && ML > 0;
+    if constexpr (!kSpread) issue(s + NS - 1, nst);
     if constexpr (ML == 0) return;
+    int li = 0;  // spread refill loads issued so far
     const uint4* st = smem + (s % NS) * kStage;
     // two-stage rings run three blocks per CU: one half's fragments at a time
     constexpr int KB = NS >= 3 ? 2 : 1;
@@ -532,8 +552,19 @@ __device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, i
         for (int n = 0; n < 4; ++n) {
           acc[m][n] = mfma32(af[ks][m], bfr[ks][n], acc[m][n]);
           if constexpr (C::AHL) acc[m][n] = mfma32(afl[ks][m], bfr[ks][n], acc[m][n]);
+          if constexpr (kSpread) {  // kNL loads evenly over the step's 8 ML tile groups
+            const int mi = (ks * ML + m) * 4 + n;
+            if ((mi + 1) * kNL / (8 * ML) > li) {  // constant once unrolled
+              __builtin_amdgcn_sched_barrier(0);
+              issue_one(s + NS - 1, nst, li);
+              ++li;
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
         }
     }
+    if constexpr (kSpread)
+      while (li < kNL) issue_one(s + NS - 1, nst, li++);
   };
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) issue(i, smem + i * kStage);
