@@ -478,6 +478,9 @@ def test_deterministic_and_workspace_reuse(orc, B):
     dict(T=300, H=1024, E=64, k=8, I=512, I_shared=512, bias="zipf"),
     dict(T=200, H=96, E=8, k=2, I=96, I_shared=0),               # K not a multiple of 64, no shared
     dict(T=129, H=2048, E=256, k=8, I=512, I_shared=512),        # Qwen shapes, one row past a tile
+    dict(T=40, H=256, E=1, k=1, I=128, I_shared=64),             # one expert
+    dict(T=24, H=128, E=4, k=4, I=64, I_shared=0),               # every expert chosen (k = E)
+    dict(T=33, H=256, E=1024, k=16, I=64, I_shared=32),          # max E and k: 1024 groups, 528 slots
 ])
 def test_prefill_small_bf16(orc, B, kw):
     say(f"[prefill] {kw}")
