@@ -503,6 +503,8 @@ def test_prefill_f32_out(orc, B):
     dict(T=160, H=1024, E=4, k=2, I=512, I_shared=512, bias="zipf"),    # hot experts span 2 tiles
     dict(T=200, H=96, E=8, k=2, I=96, I_shared=0),                    # no shared expert
     dict(T=20, H=2560, E=16, k=4, I=768, I_shared=768),               # Ling widths
+    dict(T=40, H=256, E=1, k=1, I=128, I_shared=64),                  # one expert
+    dict(T=24, H=128, E=4, k=4, I=64, I_shared=0),                    # k = E
 ])
 def test_prefill_small_mxfp4(orc, B, kw):
     """MXFP4 experts on the grouped-GEMM path: codes and scales unpacked to bf16 on the way
@@ -646,6 +648,8 @@ def test_qwen_int4_decode_full_size(orc, B, T, out):
     dict(T=64, H=512, E=32, k=4, I=192, I_shared=64, bias="zipf"),    # ragged tiles, skewed load
     dict(T=200, H=128, E=8, k=2, I=128, I_shared=0),                  # no shared expert
     dict(T=129, H=2048, E=64, k=8, I=512, I_shared=512, bias="zipf"),  # Qwen widths, a tile boundary
+    dict(T=40, H=256, E=1, k=1, I=128, I_shared=64),                  # one expert
+    dict(T=24, H=128, E=4, k=4, I=64, I_shared=0),                    # k = E
 ])
 def test_int4_prefill_small(orc, B, kw):
     """Group-wise affine 4-bit experts on the grouped-GEMM path: codes staged like MXFP4, each
