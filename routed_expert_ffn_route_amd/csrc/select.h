@@ -132,9 +132,9 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // the candidates' next digit in a 256-bin LDS histogram (hist: 512 words private to the
 // wave), a prefix sum over the bins taken from the largest digit down locates the digit that
 // holds the k-th key, and the candidates narrow to that digit; the search stops as soon as
-// that digit's whole bin is taken.  Ties at the threshold go to the lowest indices; every
-// lane places its chosen experts by a prefix count of the chosen bits.  Lanes write
-// ids_out[pos] and w_out[pos] for pos < k.
+// that digit's whole bin is taken.  Ties at the threshold go to the lowest indices; the
+// chosen experts are placed in ascending id by a prefix count of the chosen bits.  Lane
+// l < k writes ids_out[l] and w_out[l].
 template <int NV>
 __device__ __forceinline__ void select_set_nv(const float* lrow, int E, int k, int lane, unsigned* hist,
                                               int* ids_out, float* w_out) {
@@ -194,41 +194,53 @@ __device__ __forceinline__ void select_set_nv(const float* lrow, int E, int k, i
     prefix = (prefix << 8) | (uint32_t)(255 - (4 * L + j));
     if (c == need) break;  // the whole bin is taken: no tie inside it to resolve
   }
-  // chosen: (key >> shift) above prefix, plus the lowest-index `need` keys equal to it
+  // chosen: (key >> shift) above prefix, plus the lowest-index `need` keys equal to it (one
+  // ballot each; a per-lane rank only when the threshold's ties outnumber the keys still wanted)
   int quota = need;
   uint64_t chosen[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const uint32_t kh = key[i] >> shift;
+    const uint64_t gt = __ballot(ok[i] && kh > prefix);
     const uint64_t eq = __ballot(ok[i] && kh == prefix);
-    const int my_rank = __popcll(eq & ((1ull << lane) - 1ull));
-    const bool pick = ok[i] && (kh > prefix || (kh == prefix && my_rank < quota));
-    chosen[i] = __ballot(pick);
-    quota -= __popcll(eq);
-    quota = quota < 0 ? 0 : quota;
+    const int ne = __popcll(eq);
+    uint64_t take = eq;
+    if (ne > quota) {  // uniform
+      const int my_rank = __popcll(eq & ((1ull << lane) - 1ull));
+      take = __ballot(((eq >> lane) & 1ull) && my_rank < quota);
+    }
+    chosen[i] = gt | take;
+    quota = quota > ne ? quota - ne : 0;
   }
-  // weights: exp(l - m) / sum over the chosen, m = the largest logit
-  float lmax = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if ((chosen[i] >> lane) & 1ull) lmax = fmaxf(lmax, val[i]);
-  const float m = wave_max(lmax);
-  float psum = 0.f, pv[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    pv[i] = ((chosen[i] >> lane) & 1ull) ? expf(val[i] - m) : 0.f;
-    psum += pv[i];
-  }
-  const float ps = group_sum<kWave>(psum);
+  // the k chosen (value, id) pairs, in ascending id, gathered into lanes 0..k-1 through the
+  // (now free) histogram words; weights exp(l - m) / sum over the chosen, m = the largest,
+  // reduced over those k <= 16 lanes
+  float* gv = (float*)hist;
+  int* gid = (int*)hist + kWave;
   int base = 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     if ((chosen[i] >> lane) & 1ull) {
       const int pos = base + __popcll(chosen[i] & ((1ull << lane) - 1ull));
-      ids_out[pos] = lane + kWave * i;
-      w_out[pos] = pv[i] / ps;
+      gv[pos] = val[i];
+      gid[pos] = lane + kWave * i;
     }
     base += __popcll(chosen[i]);
+  }
+  __builtin_amdgcn_wave_barrier();
+  const bool act = lane < k;
+  const float v = act ? gv[lane] : -INFINITY;
+  const int id = act ? gid[lane] : 0;
+  float m = v;  // maximum over the 16-lane row holding them
+  m = fmaxf(m, dpp_f<kDppXor1>(m));
+  m = fmaxf(m, dpp_f<kDppXor2>(m));
+  m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
+  m = fmaxf(m, dpp_f<kDppMirror>(m));
+  const float pe = act ? expf(v - m) : 0.f;
+  const float ps = group_sum<16>(pe);
+  if (act) {
+    ids_out[lane] = id;
+    w_out[lane] = pe / ps;
   }
 }
 
