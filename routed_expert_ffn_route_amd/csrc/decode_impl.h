@@ -1091,7 +1091,8 @@ void* down_fn(int gi) {
 
 int gu_epc(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : 32; }  // MXFP4, INT4G64: 32
 int dn_epc(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : 32; }
-constexpr int kMaxLdsX = 64 * 1024;  // x staged in LDS by the gate/up kernels up to this size
+constexpr int kMaxLdsX = 64 * 1024;       // one token's x always fits in LDS
+constexpr int kMaxLdsXMulti = 40 * 1024;  // several tokens' x staged in LDS up to this size
 
 template <int XT, int WT, int SWT, int TM>
 int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& hook) {
@@ -1099,10 +1100,12 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   const DevInfo dv = dev_info();
   const int S = A.T * A.k, D = S < A.E ? S : A.E;
   // x goes through LDS (its loads issued ahead of the weights, read back at LDS latency); one
-  // token's row always fits (H <= MOE_MAX_H fp32 values are 64 KiB)
+  // token's row always fits (H <= MOE_MAX_H fp32 values are 64 KiB).  Several tokens' rows
+  // only up to 40 KiB: beyond that the LDS they take costs the gate/up kernel more occupancy
+  // than the staging saves, and x is read through the L1 instead
   const size_t xbytes = (size_t)A.T * A.H * (XT == MOE_F32 ? 4 : 2);
   static_assert((size_t)MOE_MAX_H * 4 <= (size_t)kMaxLdsX, "a single token's x fits in LDS");
-  const bool xl = TM == 1 || xbytes <= kMaxLdsX;
+  const bool xl = TM == 1 || xbytes <= kMaxLdsXMulti;
   // 4-bit experts read x from padded LDS rows (16 bytes after every 64)
   constexpr bool w4 = WT == MOE_MXFP4 || WT == MOE_INT4G64;
   const size_t xbytes_gu = w4 ? xbytes / 4 * 5 : xbytes;
