@@ -476,9 +476,14 @@ __device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, i
     if (A.rbias && A.bias_stride == 0 && e < A.E) bias_e = A.rbias[e];
   }
 
+  // 4-bit gate/up: every wave takes all 128 rows and 32 activation columns (its gate and its up
+  // tile), so each B fragment is unpacked by one wave instead of two
+  constexpr bool W14 = F4 && MODE == 0;
+  constexpr int MT = W14 ? 4 : 2, NTW = W14 ? 2 : 4;  // MFMA tiles per wave: rows, columns
+  const int mrow0 = W14 ? 0 : wm * 64;
   // rows of this wave that hold data (uniform): skip MFMA tiles wholly past the tile end
-  const int mlive = min(2, max(0, (nrows - wm * 64 + 31) / 32));
-  f32x16_t acc[2][4] = {};
+  const int mlive = min(MT, max(0, (nrows - mrow0 + 31) / 32));
+  f32x16_t acc[MT][NTW] = {};
   // One K-step: wait for its stage, refill the ring, then the fragment reads of the step (both
   // 16-deep halves, or one half at a time with a two-stage ring) before their MFMAs, so that
   // the reads' latency overlaps the first MFMAs.  The precise down GEMM (two MFMAs per tile)
@@ -500,19 +505,21 @@ __device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, i
     constexpr int KB = NS >= 3 ? 2 : 1;
 #pragma unroll
     for (int kb = 0; kb < 2; kb += KB) {
-    bf16x8_t af[2][2], afl[2][2], bfr[2][4];
+    bf16x8_t af[2][MT], afl[2][MT], bfr[2][NTW];
 #pragma unroll
     for (int ks = kb; ks < kb + KB; ++ks) {
       const int c = ks * 2 + (lane >> 5);
 #pragma unroll
       for (int m = 0; m < ML; ++m) {
-        af[ks][m] = __builtin_bit_cast(bf16x8_t, st[swz_unit(wm * 64 + m * 32 + (lane & 31), c)]);
+        af[ks][m] = __builtin_bit_cast(bf16x8_t, st[swz_unit(mrow0 + m * 32 + (lane & 31), c)]);
         if constexpr (C::AHL)
-          afl[ks][m] = __builtin_bit_cast(bf16x8_t, st[C::kUnitsA + swz_unit(wm * 64 + m * 32 + (lane & 31), c)]);
+          afl[ks][m] = __builtin_bit_cast(bf16x8_t, st[C::kUnitsA + swz_unit(mrow0 + m * 32 + (lane & 31), c)]);
       }
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int br = wn * 128 + n * 32 + (lane & 31);
+      for (int n = 0; n < NTW; ++n) {
+        // W14: the wave's gate rows (n = 0) and up rows (n = 1) of activation columns
+        // n0 + 32 wave ... + 31, which sit in B rows 128 (wave / 2) + 32 (wave % 2) + 64 n + i
+        const int br = W14 ? (wave >> 1) * 128 + (wave & 1) * 32 + n * 64 + (lane & 31) : wn * 128 + n * 32 + (lane & 31);
         if constexpr (I4) {  // 8 codes -> bf16(s * q + b), the group's scale and bias (one group per 2 steps)
           const uint32_t q = ((const uint32_t*)(st + kStageA + br))[c];
           const uint8_t* sp = s_sc + (br >> 6) * wtot + (br & 63) * sb + 2 * ((s0 + s) >> 1);
@@ -549,12 +556,12 @@ __device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, i
 #pragma unroll
       for (int m = 0; m < ML; ++m)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
+        for (int n = 0; n < NTW; ++n) {
           acc[m][n] = mfma32(af[ks][m], bfr[ks][n], acc[m][n]);
           if constexpr (C::AHL) acc[m][n] = mfma32(afl[ks][m], bfr[ks][n], acc[m][n]);
-          if constexpr (kSpread) {  // kNL loads evenly over the step's 8 ML tile groups
-            const int mi = (ks * ML + m) * 4 + n;
-            if ((mi + 1) * kNL / (8 * ML) > li) {  // constant once unrolled
+          if constexpr (kSpread) {  // kNL loads evenly over the step's 2 NTW ML tile groups
+            const int mi = (ks * ML + m) * NTW + n;
+            if ((mi + 1) * kNL / (2 * NTW * ML) > li) {  // constant once unrolled
               __builtin_amdgcn_sched_barrier(0);
               issue_one(s + NS - 1, nst, li);
               ++li;
@@ -571,12 +578,30 @@ __device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, i
   typedef std::integral_constant<int, 0> ML0;
   typedef std::integral_constant<int, 1> ML1;
   typedef std::integral_constant<int, 2> ML2;
-  if (mlive == 2)  // uniform
-    for (int s = 0; s < nk; ++s) step(ML2{}, s);
-  else if (mlive == 1)
-    for (int s = 0; s < nk; ++s) step(ML1{}, s);
-  else
-    for (int s = 0; s < nk; ++s) step(ML0{}, s);
+  typedef std::integral_constant<int, 3> ML3;
+  typedef std::integral_constant<int, 4> ML4;
+  auto run_k = [&](auto ml_c) {
+    for (int s = 0; s < nk; ++s) step(ml_c, s);
+  };
+  if constexpr (W14) {
+    if (mlive == 4)  // uniform
+      run_k(ML4{});
+    else if (mlive == 3)
+      run_k(ML3{});
+    else if (mlive == 2)
+      run_k(ML2{});
+    else if (mlive == 1)
+      run_k(ML1{});
+    else
+      run_k(ML0{});
+  } else {
+    if (mlive == 2)  // uniform
+      run_k(ML2{});
+    else if (mlive == 1)
+      run_k(ML1{});
+    else
+      run_k(ML0{});
+  }
   wait_vm<0>();  // no load may still write this block's LDS after it retires
 
   // ---- epilogue; C row = wm * 64 + m * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4
@@ -640,22 +665,23 @@ __device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, i
       __syncthreads();  // every wave is done with the ring (or with the previous pass)
       if (kHalves == 1 || wm == hp) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < MT; ++m) {
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
-            const int row0 = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+            const int row0 = mrow0 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
             const int row = row0 + (odd ? 1 : 0);
             uint32_t* crow = (uint32_t*)(ct + (row - hp * HR) * LDW) + ((lane & 31) >> 1);
             if constexpr (MODE == 0) {
+              // gate tile pr, up tile NTW / 2 + pr; W14: one pair at columns 32 wave ...
 #pragma unroll
-              for (int pr = 0; pr < 2; ++pr) {
-                float a = silu_fast(acc[m][pr][r]) * acc[m][2 + pr][r];
-                float b = silu_fast(acc[m][pr][r + 1]) * acc[m][2 + pr][r + 1];
+              for (int pr = 0; pr < NTW / 2; ++pr) {
+                float a = silu_fast(acc[m][pr][r]) * acc[m][NTW / 2 + pr][r];
+                float b = silu_fast(acc[m][pr][r + 1]) * acc[m][NTW / 2 + pr][r + 1];
                 if (P && pl == 1) {  // the lo parts: what bf16 rounding left out (exact in fp32)
                   a -= bf16_to_f32(f32_to_bf16(a));
                   b -= bf16_to_f32(f32_to_bf16(b));
                 }
-                crow[(wn * 64 + pr * 32) / 2] = pair_pack(a, b, odd);
+                crow[((W14 ? wave * 32 : wn * 64) + pr * 32) / 2] = pair_pack(a, b, odd);
               }
             } else {
               const float wa = row0 < nrows ? s_wt[row0] : 0.f, wb = row0 + 1 < nrows ? s_wt[row0 + 1] : 0.f;
