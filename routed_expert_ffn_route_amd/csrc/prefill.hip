@@ -476,9 +476,10 @@ __device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, i
     if (A.rbias && A.bias_stride == 0 && e < A.E) bias_e = A.rbias[e];
   }
 
-  // 4-bit gate/up: every wave takes all 128 rows and 32 activation columns (its gate and its up
-  // tile), so each B fragment is unpacked by one wave instead of two
-  constexpr bool W14 = F4 && MODE == 0;
+  // 4-bit weights: every wave takes all 128 rows and its own 64 B rows (gate/up: the gate and
+  // up tiles of 32 activation columns; down: 64 output columns), so each B fragment is
+  // unpacked by one wave instead of two
+  constexpr bool W14 = F4;
   constexpr int MT = W14 ? 4 : 2, NTW = W14 ? 2 : 4;  // MFMA tiles per wave: rows, columns
   const int mrow0 = W14 ? 0 : wm * 64;
   // rows of this wave that hold data (uniform): skip MFMA tiles wholly past the tile end
@@ -517,9 +518,12 @@ __device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, i
       }
 #pragma unroll
       for (int n = 0; n < NTW; ++n) {
-        // W14: the wave's gate rows (n = 0) and up rows (n = 1) of activation columns
-        // n0 + 32 wave ... + 31, which sit in B rows 128 (wave / 2) + 32 (wave % 2) + 64 n + i
-        const int br = W14 ? (wave >> 1) * 128 + (wave & 1) * 32 + n * 64 + (lane & 31) : wn * 128 + n * 32 + (lane & 31);
+        // W14 gate/up: the wave's gate rows (n = 0) and up rows (n = 1) of activation columns
+        // n0 + 32 wave ... + 31, which sit in B rows 128 (wave / 2) + 32 (wave % 2) + 64 n + i;
+        // W14 down: B rows 64 wave + 32 n + i
+        const int br = !W14 ? wn * 128 + n * 32 + (lane & 31)
+                       : MODE == 0 ? (wave >> 1) * 128 + (wave & 1) * 32 + n * 64 + (lane & 31)
+                                   : wave * 64 + n * 32 + (lane & 31);
         if constexpr (I4) {  // 8 codes -> bf16(s * q + b), the group's scale and bias (one group per 2 steps)
           const uint32_t q = ((const uint32_t*)(st + kStageA + br))[c];
           const uint8_t* sp = s_sc + (br >> 6) * wtot + (br & 63) * sb + 2 * ((s0 + s) >> 1);
@@ -628,16 +632,16 @@ __device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, i
     // precise down: fp32 weighted rows straight from the accumulators; lanes 0-31 and 32-63
     // of a store hold 32 consecutive columns of two rows, two whole 128-byte pieces
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < MT; ++m) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+        const int row = mrow0 + m * 32 + 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
         if (row >= nrows) continue;
         const float wt = s_wt[row];
         float* orow = L.outf + (size_t)s_slot[row] * A.H;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const int col = n0 + wn * 128 + n * 32 + (lane & 31);
+        for (int n = 0; n < NTW; ++n) {
+          const int col = n0 + (W14 ? wave * 64 : wn * 128) + n * 32 + (lane & 31);
           if (col < N) orow[col] = wt * acc[m][n][r];
         }
       }
@@ -686,8 +690,9 @@ __device__ __forceinline__ void pf_gemm_body(const Args& A, const PfLayout& L, i
             } else {
               const float wa = row0 < nrows ? s_wt[row0] : 0.f, wb = row0 + 1 < nrows ? s_wt[row0 + 1] : 0.f;
 #pragma unroll
-              for (int n = 0; n < 4; ++n)
-                crow[(wn * 128 + n * 32) / 2] = pair_pack(wa * acc[m][n][r], wb * acc[m][n][r + 1], odd);
+              for (int n = 0; n < NTW; ++n)
+                crow[((W14 ? wave * 64 : wn * 128) + n * 32) / 2] =
+                    pair_pack(wa * acc[m][n][r], wb * acc[m][n][r + 1], odd);
             }
           }
         }
