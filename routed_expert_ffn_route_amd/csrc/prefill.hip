@@ -4,7 +4,8 @@
 //           split into three bf16 parts (hi + mid + lo == w) by a small pass, so each product
 //           is exact and the three partial sums are added in fp32 -- fp32-accurate logits at
 //           bf16 matrix-core rates.
-//  select   one wave per token (descending rank, ties to the lower index).
+//  select   one wave per token: the K-split partial logits added in split order, then the k
+//           largest (ties to the lower index; ranked when the routing is an output).
 //  permute  histogram of assignments per expert -> prefix scan -> scatter of slots into expert
 //           groups -> block map of fixed-size row tiles ("Optimizing on-device inference for
 //           Apple Silicon", section "Keep expert routing on the GPU"; the shared expert is one
@@ -24,9 +25,11 @@
 // against the exactly dequantised layer, which bf16 activations and bf16 slot rows (each
 // rounding costs about 1e-3 on its own) would not meet.
 //
-// All three GEMMs run one kernel, pf_gemm: 128 x 256 block tiles, K-steps of 32 staged in
-// a three-deep LDS ring that the buffer unit fills directly (loads to LDS, no register
-// staging), rows XOR-swizzled so that MFMA fragment reads are free of bank conflicts.
+// The router, gate/up and down GEMMs share one block body (pf_gemm_body): 128 x 256 block
+// tiles, K-steps of 32 staged in a two- or three-deep LDS ring that the buffer unit fills
+// directly (loads to LDS, no register staging), rows XOR-swizzled so that MFMA fragment reads
+// are free of bank conflicts.  W4A8's routed tiles run their own body on the block-scaled
+// fp8 x fp4 matrix cores.
 #include <algorithm>
 #include <type_traits>
 
@@ -210,7 +213,9 @@ __global__ __launch_bounds__(256) void pf_split_router(Args A, uint16_t* planes)
 // ------------------------------------------------------------------------------------------
 // Grouped GEMM.  A block computes a BM-row x 256-column tile of C = A . B^T (B rows are
 // output columns, K contiguous); BM / 32 waves in a (BM / 64) x 2 grid own 64 x 128 each
-// (2 x 4 MFMA 32x32x16 tiles).  Operands are read through buffer resources: an offset at or past a
+// (2 x 4 MFMA 32x32x16 tiles), except with 4-bit weights, where each of the four waves owns all
+// 128 rows and 64 B rows of its own (4 x 2 tiles), so that every weight fragment is unpacked
+// by one wave.  Operands are read through buffer resources: an offset at or past a
 // resource's size reads as zero (kOOB), which masks rows past the tile or matrix end.
 // Each K-step of 32 lands in one of NS LDS stages via buffer loads to LDS (every lane
 // writes its 16 bytes at stage base + 16 * lane); 16-byte chunk c of row r sits at unit
@@ -219,9 +224,9 @@ __global__ __launch_bounds__(256) void pf_split_router(Args A, uint16_t* planes)
 // one), so fragment reads are free of bank conflicts.  Step s + NS - 1 is requested before
 // step s is multiplied: one barrier per step.
 //
-// MODE 0 gate/up: A = gathered token rows of x; B rows per wave column half wn are, in 32-row
-//        groups, gate / up / gate / up of the activation columns n0 + 64 wn ... + 63; the
-//        epilogue applies SwiGLU in registers and stores bf16 activations.
+// MODE 0 gate/up: A = gathered token rows of x; the B rows of column half h are 64 gate rows
+//        and then 64 up rows of the activation columns n0 + 64 h ... + 63; the epilogue
+//        applies SwiGLU in registers and stores bf16 activations.
 // MODE 1 down: A = activation rows of the tile; B = Wd rows n0 ...; the epilogue scales by
 //        the slot's routing weight and stores bf16 at the slot's row.
 // MODE 2 router: A = token rows t0 ...; B rows per wave column half are the hi / mid / lo
