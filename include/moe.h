@@ -80,7 +80,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2, MOE_INT4G64 = 3 } moe_d
 #define MOE_MAX_H 16384    /* hidden size                                      */
 #define MOE_MAX_I 8192     /* intermediate sizes                               */
 /* T > 16 (grouped-GEMM path) additionally needs bf16 activations, T * H * 2 < 2^31 bytes
-   of x and, with MXFP4 experts, H <= 8192 and I <= 8192 (a tile's scale rows sit in LDS). */
+   of x and, with 4-bit experts, GEMM launches whose LDS fits the CU's 160 KiB: each wave
+   stages its weight rows' scale block (INT4G64: and bias block) for the whole reduction, so
+   MXFP4 (and W4A8) take H, I <= 8192 and INT4G64 H <= 7680, I <= 6144. */
 
 typedef struct {
   int32_t T;            /* tokens, >= 1                                        */

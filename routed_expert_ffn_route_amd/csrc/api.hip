@@ -45,6 +45,10 @@ int check_shape(const moe_shape_t* s) {
     if ((s->expert_dtype == MOE_MXFP4 || s->expert_dtype == MOE_INT4G64) && (s->H > 8192 || s->I > 8192))
       return MOE_EUNSUPPORTED;
     if ((size_t)s->T * s->H * 2 >= ((size_t)1 << 31)) return MOE_EUNSUPPORTED;  // 32-bit row offsets
+    // the GEMM launches' LDS (4-bit experts: the ring plus one scale block per wave), with the
+    // down kernels' 2 KiB of static LDS (a tile's slots and routing weights)
+    if (prefill_lds_bytes(s->H, s->I, s->I_shared, s->expert_dtype, s->act_quant == MOE_QMXFP8) + 2048 > kCuLdsBytes)
+      return MOE_EUNSUPPORTED;
   }
   return MOE_OK;
 }

@@ -60,6 +60,11 @@ int launch_stage_probe(const void* buf, uint32_t mask, int seg, int iters, uint3
 // Workspace bytes needed by the prefill path's sections; precise: MXFP4 or INT4G64 experts
 // (activations as bf16 hi + lo parts, fp32 slot rows).
 size_t prefill_ws_bytes(int T, int H, int E, int k, int I, int Is, bool precise, bool w4a8);
+// Largest dynamic LDS of the prefill GEMM launches for these sizes (4-bit experts stage one
+// scale block per wave and tile, which grows with the reduction length); shapes whose launches
+// would not fit kCuLdsBytes are rejected before anything is launched.
+size_t prefill_lds_bytes(int H, int I, int Is, int wdt, bool w4a8);
+constexpr size_t kCuLdsBytes = 160 * 1024;  // LDS per CU (gfx950)
 int prefill_tiles_cap(int T, int E, int k);
 constexpr int kPfTileRows = 128;  // rows per grouped-GEMM tile (the block map's unit)
 

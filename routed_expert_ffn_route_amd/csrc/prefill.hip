@@ -1185,7 +1185,31 @@ size_t pf_lds(int K) {
   const size_t epi = (MODE == 1 && P) ? 0 : (size_t)kPfBM * ((MODE == 0 ? kPfBN / 2 : kPfBN) + 8) * 2;
   return std::max(C::ring_bytes + sc, epi);
 }
+// W4A8 LDS: the ring, the four waves' B scale blocks, the tile's A scale rows
+size_t pf_w4a8_lds(int K) {
+  const size_t ring = (size_t)kPfNS * (kPfBM * 64 + kPfBN * 32);
+  return ring + (size_t)4 * ((64 * (K / 32) + 1023) / 1024) * 1024 + (size_t)kPfBM * mx8_scale_ld(K);
+}
 }  // namespace
+
+size_t prefill_lds_bytes(int H, int I, int Is, int wdt, bool w4a8) {
+  size_t gu = 0, dn = 0;
+  if (w4a8 || wdt == MOE_MXFP4 || wdt == MOE_INT4G64) {  // one launch: shared (bf16 precise) + routed tiles
+    gu = pf_lds<0, kMixNsShared<0>, MOE_BF16, true>(H);  // as the launches size it
+    dn = pf_lds<1, kMixNsShared<1>, MOE_BF16, true>(Is);
+    if (w4a8) {
+      gu = std::max(gu, pf_w4a8_lds(H));
+      dn = std::max(dn, pf_w4a8_lds(I));
+    } else if (wdt == MOE_INT4G64) {
+      gu = std::max(gu, pf_lds<0, kPfNS, MOE_INT4G64, true>(H));
+      dn = std::max(dn, pf_lds<1, kPfNS, MOE_INT4G64, true>(I));
+    } else {
+      gu = std::max(gu, pf_lds<0, kPfNS, MOE_MXFP4, true>(H));
+      dn = std::max(dn, pf_lds<1, kPfNS, MOE_MXFP4, true>(I));
+    }
+  }
+  return std::max(gu, dn);  // bf16 experts: static LDS only (fixed by the tile, below the limit)
+}
 
 int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   PfLayout L = pf_layout(A);
@@ -1197,11 +1221,6 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
   const int cap = prefill_tiles_cap(A.T, A.E, A.k);
   const int Imax = A.I > A.Is ? A.I : A.Is;
   const bool f4 = A.wdt == MOE_MXFP4, i4 = A.wdt == MOE_INT4G64, w4a8 = A.aq == MOE_QMXFP8;
-  // W4A8 LDS: the ring, the four waves' B scale blocks, the tile's A scale rows
-  auto w4a8_lds = [&](int K) {
-    const size_t ring = (size_t)kPfNS * (kPfBM * 64 + kPfBN * 32);
-    return ring + (size_t)4 * ((64 * (K / 32) + 1023) / 1024) * 1024 + (size_t)kPfBM * mx8_scale_ld(K);
-  };
   if (w4a8) {  // x -> MXFP8 for the routed gate/up GEMM
     void* aq[] = {&A, &L};
     if (launch(hook, "pf_quant_x", (const void*)pf_quant_x, dim3((unsigned)(((size_t)A.T * (A.H / 32) + 255) / 256)),
@@ -1233,7 +1252,7 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
     const int nbt = (Imax + kPfBN / 2 - 1) / (kPfBN / 2);
     const size_t lsh = pf_lds<0, kMixNsShared<0>, MOE_BF16, true>(A.H);
     if (w4a8)
-      rc = run_mix("pf_gateup", (const void*)pf_gemm_mix<0, MOE_MXFP4, true>, nbt, std::max(w4a8_lds(A.H), lsh));
+      rc = run_mix("pf_gateup", (const void*)pf_gemm_mix<0, MOE_MXFP4, true>, nbt, std::max(pf_w4a8_lds(A.H), lsh));
     else if (i4)
       rc = run_mix("pf_gateup", (const void*)pf_gemm_mix<0, MOE_INT4G64, false>, nbt,
                    std::max(pf_lds<0, kPfNS, MOE_INT4G64, true>(A.H), lsh));
@@ -1248,7 +1267,7 @@ int launch_prefill(Args A, hipStream_t st, const LaunchHook& hook) {
     const int nbt = (A.H + kPfBN - 1) / kPfBN;
     const size_t lsh = pf_lds<1, kMixNsShared<1>, MOE_BF16, true>(A.Is);
     if (w4a8)
-      rc = run_mix("pf_down", (const void*)pf_gemm_mix<1, MOE_MXFP4, true>, nbt, std::max(w4a8_lds(A.I), lsh));
+      rc = run_mix("pf_down", (const void*)pf_gemm_mix<1, MOE_MXFP4, true>, nbt, std::max(pf_w4a8_lds(A.I), lsh));
     else if (i4)
       rc = run_mix("pf_down", (const void*)pf_gemm_mix<1, MOE_INT4G64, false>, nbt,
                    std::max(pf_lds<1, kPfNS, MOE_INT4G64, true>(A.I), lsh));

@@ -67,6 +67,10 @@ def test_strerror_covers_codes(lib):
     (dict(T=64, expert_dtype=2, I=8192 + 32), B.MOE_EUNSUPPORTED),
     # group-wise affine 4-bit: groups of 64 along H and I
     (dict(expert_dtype=3, H=2048 + 32), B.MOE_EUNSUPPORTED), (dict(expert_dtype=3, I=512 + 32), B.MOE_EUNSUPPORTED),
+    # ... and on the grouped-GEMM path a wave's scale and bias blocks must fit in LDS beside the
+    # ring (H <= 7680 for gate/up, I <= 6144 for down)
+    (dict(T=64, expert_dtype=3, H=7680 + 64), B.MOE_EUNSUPPORTED),
+    (dict(T=64, expert_dtype=3, I=6144 + 64), B.MOE_EUNSUPPORTED),
     (dict(expert_dtype=3, act_dtype=0, shared_dtype=0), B.MOE_EUNSUPPORTED),
     # W4A8: MXFP4 experts on the grouped-GEMM path only
     (dict(T=64, act_quant=1), B.MOE_EUNSUPPORTED), (dict(T=4, expert_dtype=2, act_quant=1), B.MOE_EUNSUPPORTED),
@@ -85,6 +89,8 @@ def test_workspace_sizes_and_paths(lib):
                      (dict(T=4096, H=2560, E=512, I=768, I_shared=768, expert_dtype=2, out_dtype=0),
                       "prefill.mxfp4"), (dict(T=64, expert_dtype=2, H=8192), "prefill.mxfp4"),
                      (dict(expert_dtype=3), "decode.int4g64"), (dict(T=4096, expert_dtype=3), "prefill.int4g64"),
+                     (dict(T=64, expert_dtype=3, H=7680, I=6144), "prefill.int4g64"),
+                     (dict(T=4, expert_dtype=3, H=16384, I=8192), "decode.int4g64"),
                      (dict(T=4096, expert_dtype=2, out_dtype=0, act_quant=1), "prefill.mxfp4.w4a8"),
                      (dict(T=4, H=256, E=16, k=2, I=128, I_shared=128, act_dtype=0, expert_dtype=0,
                            shared_dtype=0, out_dtype=0), "decode.f32")]:

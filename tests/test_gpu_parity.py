@@ -336,6 +336,32 @@ def test_decode_edge_shapes_bf16(orc, B, kw):
     full_check(orc, B, Lh, xh, Ld, xd, f"edge {kw}")
 
 
+# The largest hidden and intermediate sizes the library accepts (H <= 16384, I <= 8192; on the
+# grouped-GEMM path MXFP4 H, I <= 8192 and INT4G64 H <= 7680, I <= 6144, so that every wave's
+# scale blocks fit in LDS), on both paths, with small T and E so that the oracle finishes in
+# seconds.
+@pytest.mark.parametrize("kw", [
+    dict(T=1, H=16384, E=8, k=2, I=128, I_shared=64),                   # x (32 KiB) staged in LDS
+    dict(T=4, H=16384, E=8, k=2, I=128, I_shared=64),                   # x (128 KiB) through the L1
+    dict(T=1, H=16384, E=4, k=2, I=64, I_shared=32, act="f32", expert="f32", shared="f32", out="f32"),
+                                                                        # fp32 x: 64 KiB, all of LDS
+    dict(T=4, H=256, E=8, k=2, I=8192, I_shared=8192),                  # down over I = 8192
+    dict(T=4, H=16384, E=8, k=2, I=128, I_shared=64, expert="mxfp4", out="f32"),
+    dict(T=3, H=256, E=8, k=2, I=8192, I_shared=256, expert="int4g64"),
+    dict(T=40, H=16384, E=4, k=2, I=128, I_shared=64),                  # prefill, H = 16384
+    dict(T=40, H=256, E=4, k=2, I=8192, I_shared=8192),                 # prefill, I = 8192
+    dict(T=24, H=8192, E=4, k=2, I=256, I_shared=64, expert="mxfp4", out="f32"),
+    dict(T=24, H=512, E=4, k=2, I=8192, I_shared=64, expert="mxfp4", out="f32"),
+    dict(T=24, H=7680, E=4, k=2, I=256, I_shared=64, expert="int4g64"),
+    dict(T=24, H=512, E=4, k=2, I=6144, I_shared=64, expert="int4g64"),
+])
+def test_max_hidden_and_intermediate(orc, B, kw):
+    say(f"[max-size] {kw}")
+    Lh, xh = synth.make_layer(**kw, seed=13)
+    Ld, xd = synth.to_device(Lh, xh)
+    full_check(orc, B, Lh, xh, Ld, xd, f"max {kw}")
+
+
 def test_decode_fp32_single_token(orc, B):
     say("[decode-f32-T1]")
     Lh, xh = synth.make_layer(1, 512, 32, 4, 128, 96, "f32", "f32", "f32", "f32", seed=6)
