@@ -739,10 +739,17 @@ __global__ __launch_bounds__(kThreads) void dec_gateup(Args A, int tiles, int sh
 // weight chunks with the next item's loads in flight while it consumes the current one.  Per
 // (row group, wave) partial sums are added up in LDS and summed over the waves in a fixed
 // order at the end, so the result is deterministic.
-// Dynamic LDS (4-byte words): plan (2D + 2DT), partials [nrgb_max][NW][TM][RB], then ALDS
-// activations [T*k][I] at act_off and [T][Is] at ash_off.
-template <int WT, int SWT, int G, int NCH, int TM, bool ALDS>
-__global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, int act_off, int ash_off) {
+// PH (several tokens, when all routed rows do not fit): the distinct experts are taken in
+// phases, each as many consecutive experts as their token rows fit act_rows staged rows; a
+// phase stages its rows (expert u's tokens at rows s_base[u] + the token's rank in u's mask),
+// runs its items, and the next one restages behind a barrier.  The shared items and rows stay
+// for the whole kernel (phase 0 runs the shared items).
+// Dynamic LDS (4-byte words): plan (2D + 2DT; PH: + D expert bases + act_rows row slots),
+// partials [nrgb_max][NW][TM][RB], then ALDS activations [T*k][I] (PH: [act_rows][I]) at
+// act_off and [T][Is] at ash_off.
+template <int WT, int SWT, int G, int NCH, int TM, bool ALDS, bool PH = false>
+__global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, int act_off, int ash_off,
+                                                 int act_rows) {
   extern __shared__ float s_f[];
   static_assert(sizeof(typename DN<WT>::W) == 16 && sizeof(typename DN<SWT>::W) == 16, "16-byte chunks");
   constexpr int RB = kWave / G;
@@ -755,7 +762,9 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
   unsigned* s_m = (unsigned*)(s_f + D);
   int* s_sl = (int*)(s_f + 2 * D);
   float* s_w = s_f + 2 * D + D * T;
-  float* s_part = s_f + 2 * D + 2 * D * T;
+  int* s_base = (int*)(s_f + 2 * D + 2 * D * T);  // PH
+  int* s_rowslot = s_base + D;                     // PH
+  float* s_part = s_f + 2 * D + 2 * D * T + (PH ? D + act_rows : 0);
   float* s_act = s_f + act_off;
   float* s_ash = s_f + ash_off;
 
@@ -779,13 +788,14 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
   for (int t = 0; t < TM; ++t) acc[t] = 0.f;
   int cur_j = -1;
   int nd = 0, per_rg = 0;  // routed items per row group, known once the plan is read
+  int u0 = 0, nup = 0, qs = nqs;  // the phase's first expert, its expert count, its shared items
   struct Buf {
     uint4 w[NCH];
     uint32_t sb[NCH];
   };
   auto row_of = [&](int j) { return ((int)blockIdx.x + j * (int)gridDim.x) * RB + grp; };
   auto load = [&](int q, Buf& bf) {
-    if (q < nqs) {  // uniform: shared item (row group j, slice sl)
+    if (q < qs) {  // uniform: shared item (row group j, slice sl)
       const int j = q / nsls, sl = q - j * nsls;
       const int h = row_of(j), hh = h < A.H ? h : 0;
       const uint8_t* row = (const uint8_t*)A.sdown + (size_t)hh * rbs;
@@ -798,9 +808,9 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
       }
       return;
     }
-    const int r = q - nqs;
+    const int r = q - qs;
     const int j = r / per_rg, r2 = r - j * per_rg;
-    const int sl = r2 / nd, u = r2 - sl * nd;
+    const int sl = r2 / nup, u = u0 + r2 - sl * nup;
     const int h = row_of(j), hh = h < A.H ? h : 0;
     const int e = s_e[u];
     const uint8_t* row = (const uint8_t*)A.down + ((size_t)e * A.H + hh) * rb;
@@ -830,17 +840,17 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
   // registers): a shared item is every token with weight 1 over a_sh's rows
   const unsigned all_t = (T >= 32) ? 0xffffffffu : ((1u << T) - 1u);
   auto consume = [&](int q, const Buf& bf) {
-    const bool sh = q < nqs;  // uniform
+    const bool sh = q < qs;  // uniform
     int j, sl, u = 0;
     if (sh) {
       j = q / nsls;
       sl = q - j * nsls;
     } else {
-      const int r = q - nqs;
+      const int r = q - qs;
       j = r / per_rg;
       const int r2 = r - j * per_rg;
-      sl = r2 / nd;
-      u = r2 - sl * nd;
+      sl = r2 / nup;
+      u = u0 + r2 - sl * nup;
     }
     if (j != cur_j) {  // uniform
       flush();
@@ -866,7 +876,8 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       if (!((mask >> t) & 1u)) continue;  // uniform
-      const float* arow = ab + (size_t)(sh ? t : s_sl[u * T + t]) * ld;
+      const int ar = sh ? t : PH ? s_base[u] + __popc(mask & ((1u << t) - 1u)) : s_sl[u * T + t];
+      const float* arow = ab + (size_t)ar * ld;
       const float wt = sh ? 1.f : s_w[u * T + t];
       float part = 0.f;
 #pragma unroll
@@ -908,7 +919,7 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
     r_sl[j] = i < D * T ? P.dslot()[i] : 0;
     r_w[j] = i < D * T ? P.dw()[i] : 0.f;
   }
-  const int n4 = ALDS ? S * A.I / 4 : 0, n4s = ALDS ? T * A.Is / 4 : 0;
+  const int n4 = ALDS && !PH ? S * A.I / 4 : 0, n4s = ALDS ? T * A.Is / 4 : 0;
   float4 sv[kStg];
 #pragma unroll
   for (int j = 0; j < kStg; ++j) {
@@ -948,16 +959,59 @@ __global__ __launch_bounds__(1024) void dec_down(Args A, int nrg, int nrgb_max, 
   for (int i = tid + kStg * bd; i < n4 + n4s; i += bd)  // larger windows: the rest, pass by pass
     *stage_dst(i) = i < n4 ? ldf4(A.a + (size_t)i * 4) : ldf4(A.a_sh + (size_t)(i - n4) * 4);
   nd = *P.nd();
+  nup = nd;
   __syncthreads();
-  per_rg = nsl * nd;
-  const int nq = nqs + nrgb * per_rg;
-  const int nmine = wave < nq ? (nq - 1 - wave) / NW + 1 : 0;
-  if (nmine > 0) {  // uniform; this wave's items are q = wave + NW * step
-    if (!early) load(wave, a);
-    stream_loaded<Buf>(nmine, a, b, [&](int st, Buf& bf) { load(wave + NW * st, bf); },
-                       [&](int st, const Buf& bf) { consume(wave + NW * st, bf); });
-    flush();
+  for (int ph = 0;; ++ph) {
+    if constexpr (PH) {
+      // the phase's experts: from u0 on while their token rows fit the staged rows (the
+      // launcher makes act_rows >= T, so every phase takes at least one expert)
+      int rows = 0, u1 = u0;
+      while (u1 < nd && rows + __popc(s_m[u1]) <= act_rows) rows += __popc(s_m[u1++]);
+      if (u1 == u0) {  // not reached (act_rows >= T): one expert, its first act_rows rows
+        u1 = u0 + 1;
+        rows = act_rows;
+      }
+      nup = u1 - u0;
+      qs = ph == 0 ? nqs : 0;
+      if (ph > 0) __syncthreads();  // every wave is done with the previous phase's rows
+      if (threadIdx.x == 0) {
+        int r = 0;
+        for (int u = u0; u < u1; ++u) {
+          s_base[u] = r;
+          r += __popc(s_m[u]);
+        }
+      }
+      __syncthreads();
+      for (int i = tid; i < nup * T; i += bd) {
+        const int u = u0 + i / T, t = i - (i / T) * T;
+        const unsigned m = s_m[u];
+        const int r = s_base[u] + __popc(m & ((1u << t) - 1u));
+        if (((m >> t) & 1u) && r < act_rows) s_rowslot[r] = s_sl[u * T + t];
+      }
+      __syncthreads();
+      for (int i = tid; i < rows * q4; i += bd) {
+        const int r = i / q4, q = i - r * q4;
+        const float4 v = ldf4(A.a + (size_t)s_rowslot[r] * A.I + (size_t)q * 4);
+        if constexpr (AP)
+          *((float4*)(s_act + (size_t)r * ldr + (q >> 3) * kCS) + (q & 7)) = v;
+        else
+          *((float4*)s_act + (size_t)r * q4 + q) = v;
+      }
+      __syncthreads();
+    }
+    per_rg = nsl * nup;
+    const int nq = qs + nrgb * per_rg;
+    const int nmine = wave < nq ? (nq - 1 - wave) / NW + 1 : 0;
+    if (nmine > 0) {  // uniform; this wave's items are q = wave + NW * step
+      if (!early || ph > 0) load(wave, a);
+      stream_loaded<Buf>(nmine, a, b, [&](int st, Buf& bf) { load(wave + NW * st, bf); },
+                         [&](int st, const Buf& bf) { consume(wave + NW * st, bf); });
+    }
+    if constexpr (!PH) break;
+    u0 += nup;
+    if (u0 >= nd) break;
   }
+  flush();
   __syncthreads();
   for (int i = threadIdx.x; i < nrgb * TM * RB; i += blockDim.x) {
     const int j = i / (TM * RB), r = i - j * (TM * RB);
@@ -1079,10 +1133,10 @@ void* gateup_fn(int gi) {
   }
   return nullptr;
 }
-template <int WT, int SWT, int TM, bool ALDS>
+template <int WT, int SWT, int TM, bool ALDS, bool PH = false>
 void* down_fn(int gi) {
   switch (gi) {
-#define C(i) case i: return (void*)dec_down<WT, SWT, kDN[i].G, kDN[i].NCH, TM, ALDS>;
+#define C(i) case i: return (void*)dec_down<WT, SWT, kDN[i].G, kDN[i].NCH, TM, ALDS, PH>;
     C(0) C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8) C(9) C(10) C(11)
 #undef C
   }
@@ -1156,9 +1210,37 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   int ash_off = (int)(act_off + (act_floats + 3) / 4 * 4);
   const size_t lds_act = (size_t)ash_off * 4 + (size_t)A.T * A.Is * 4;
   const bool alds = lds_act <= (size_t)dv.max_lds;
-  const size_t lds3 = alds ? lds_act : (size_t)act_off * 4;
+  size_t lds3 = alds ? lds_act : (size_t)act_off * 4;
   void* f3 = alds ? down_fn<WT, SWT, TM, true>(g3) : down_fn<WT, SWT, TM, false>(g3);
-  void* args3[] = {&A, &nrg, &nrgb, &act_off, &ash_off};
+  int act_rows = 0;
+  if constexpr (TM >= 8 && w4) {
+    // 4-bit experts, several tokens whose routed rows do not all fit: stage them in phases of
+    // act_rows rows (at least T, one expert's worst case), the most that fit beside the shared
+    // rows.  (Read from the L2 instead, each 16-byte weight chunk would pull 128 bytes of
+    // activations per token; bf16 chunks pull 32, and they are faster without the phases.)
+    if (!alds) {
+      const size_t ldr = w4 ? (size_t)(A.I / 32) * 36 : (size_t)A.I;  // floats per staged row
+      const size_t part = (size_t)nrgb * nw * TM * rb3;
+      auto need = [&](int rows, int* ao, int* so) {
+        const size_t ao_ = (plan_w + D + rows + part + 3) / 4 * 4;
+        const size_t so_ = ao_ + ((size_t)rows * ldr + 3) / 4 * 4;
+        *ao = (int)ao_;
+        *so = (int)so_;
+        return so_ * 4 + (size_t)A.T * A.Is * 4;
+      };
+      int ao, so;
+      int rows = (int)std::min<size_t>((size_t)S, (size_t)dv.max_lds / 4 / (ldr + 1));
+      while (rows >= A.T && need(rows, &ao, &so) > (size_t)dv.max_lds) --rows;
+      if (rows >= A.T) {
+        act_rows = rows;
+        act_off = ao;
+        ash_off = so;
+        lds3 = need(rows, &ao, &so);
+        f3 = down_fn<WT, SWT, TM, true, true>(g3);
+      }
+    }
+  }
+  void* args3[] = {&A, &nrg, &nrgb, &act_off, &ash_off, &act_rows};
   err = launch(hook, "dec_down", f3, dim3(grid3), dim3(kWave * nw), args3, lds3, st);
   if (err != hipSuccess) return MOE_EHIP;
   return MOE_OK;
