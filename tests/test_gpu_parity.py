@@ -456,7 +456,9 @@ def test_ling_verify_sweep(orc, B, T, d):
     assert len(set(ids.ravel().tolist())) == d
 
 
-@pytest.mark.parametrize("T,d", [(1, None), (4, 32), (4, 20), (3, 17), (5, 33)])
+# T = 8 and 16: the routed activations exceed LDS, so the down kernel stages them in phases of
+# consecutive experts (several phases at T = 16, with the verify bias's shared experts)
+@pytest.mark.parametrize("T,d", [(1, None), (4, 32), (4, 20), (3, 17), (5, 33), (8, 48), (16, 96)])
 def test_ling_mxfp4(orc, B, T, d):
     """Ling shapes with MXFP4 experts (e2m1 codes, e8m0 scales 2^-4..2^2), bf16 activations
     and shared expert, fp32 output."""
@@ -469,7 +471,7 @@ def test_ling_mxfp4(orc, B, T, d):
 def test_mxfp4_small_shapes(orc, B):
     for kw in (dict(T=1, H=256, E=8, k=2, I=64, I_shared=64), dict(T=6, H=2048, E=16, k=4, I=512, I_shared=96),
                dict(T=16, H=2560, E=32, k=4, I=256, I_shared=64),    # x from global
-               dict(T=16, H=512, E=64, k=8, I=1024, I_shared=64)):   # activations (590 KiB) from global
+               dict(T=16, H=512, E=64, k=8, I=1024, I_shared=64)):   # activations (590 KiB) staged in phases
         say(f"[mxfp4-small] {kw}")
         Lh, xh = synth.make_layer(**kw, act="bf16", expert="mxfp4", shared="bf16", out="f32", seed=5)
         Ld, xd = synth.to_device(Lh, xh)
@@ -642,7 +644,8 @@ def test_ling_mxfp4_prefill_full_size(orc, B):
     dict(T=5, H=640, E=24, k=8, I=320, I_shared=0, out="bf16"),     # ragged rows, no shared expert
     dict(T=16, H=2560, E=32, k=4, I=256, I_shared=64, out="f32"),   # x from global (80 KiB)
     dict(T=2, H=4608, E=16, k=2, I=64, I_shared=64, out="f32"),     # a row longer than one slice
-    dict(T=16, H=512, E=64, k=8, I=1024, I_shared=64, out="bf16"),  # activations (590 KiB) from global
+    dict(T=16, H=512, E=64, k=8, I=1024, I_shared=64, out="bf16"),  # activations (590 KiB) staged in phases
+    dict(T=9, H=512, E=16, k=8, I=2048, I_shared=128, out="f32"),   # phases with many tokens per expert
 ])
 def test_int4_decode_small(orc, B, kw):
     """Group-wise affine 4-bit experts on the decode path (each weight s*q + b formed in fp32)."""
