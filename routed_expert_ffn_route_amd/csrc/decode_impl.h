@@ -1163,10 +1163,11 @@ int launch_decode_t(Args A, hipStream_t st, bool route_only, const LaunchHook& h
   // 4-bit experts read x from padded LDS rows (16 bytes after every 64)
   constexpr bool w4 = WT == MOE_MXFP4 || WT == MOE_INT4G64;
   const size_t xbytes_gu = w4 ? xbytes / 4 * 5 : xbytes;
-  // shared expert gate/up: one row per wave, in the selection kernel's blocks (T = 2..4) or
-  // beside the routed rows of the gate/up kernel (T = 1, and T > 4, where the selection
-  // kernel's blocks of 8 or 16 waves would be too few to stream it)
-  constexpr bool sh_in_sel = TM > 1 && TM <= 4;
+  // shared expert gate/up: one row per wave, in the selection kernel's blocks while a long
+  // selection (T = 2..4 tokens over E >= 512 experts) leaves time to stream it there, else
+  // beside the routed rows of the gate/up kernel (T = 1; T > 4, where the selection kernel's
+  // blocks of 8 or 16 waves would be too few; a short selection over fewer experts)
+  const bool sh_in_sel = TM > 1 && TM <= 4 && A.E >= 512;
   const int sh_waves = sh_in_sel ? TM : kWaves;
   int nsh = A.Is > 0 ? (A.Is + sh_waves - 1) / sh_waves : 0;
   void* args1[] = {&A};
