@@ -646,6 +646,8 @@ def test_ling_mxfp4_prefill_full_size(orc, B):
     dict(T=2, H=4608, E=16, k=2, I=64, I_shared=64, out="f32"),     # a row longer than one slice
     dict(T=16, H=512, E=64, k=8, I=1024, I_shared=64, out="bf16"),  # activations (590 KiB) staged in phases
     dict(T=9, H=512, E=16, k=8, I=2048, I_shared=128, out="f32"),   # phases with many tokens per expert
+    dict(T=16, H=512, E=8, k=8, I=2048, I_shared=64, out="f32"),    # every token on every expert: one
+                                                                    # expert (16 rows) per phase
 ])
 def test_int4_decode_small(orc, B, kw):
     """Group-wise affine 4-bit experts on the decode path (each weight s*q + b formed in fp32)."""
